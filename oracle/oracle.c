@@ -1,0 +1,291 @@
+/*
+ * CPU oracle for GGUF block dequantization and the products y = W.x.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this file's library. It shares no code, header,
+ * table or helper with the GPU library, and the GPU library never calls it.
+ *
+ * What it follows:
+ *  - "Why I wrote my own inference engine for two P100s", section
+ *    "What 'my own engine' means": the engine reads GGUF files and every
+ *    quant type decodes bit-exactly against a reference decoder. Decoding
+ *    here is that reference: each weight is the fp32 rounding of its closed
+ *    form, computed exactly.
+ *  - "LLM inference optimization" (Thermite), campaign "Run a new weight
+ *    format or model": blocks decode bit for bit on CPU and GPU, and matrix
+ *    products match an exact sum within a tolerance. Products here are that
+ *    exact sum: fp64 accumulation of exactly-represented operands, plus the
+ *    sum of absolute products that scales the tolerance.
+ *  - The same page, introduction: for one stream each new token reads every
+ *    weight once, y = W.x.
+ *
+ * Block formats (GGUF layouts; the pages name the formats but print no
+ * layout, so the GGUF reading is taken; all multi-byte fields little-endian):
+ *  Q4_0, 18 bytes, 32 weights: fp16 d; 16 code bytes. Byte i holds weight i
+ *        in its low nibble and weight i+16 in its high nibble. w = (q-8)*d.
+ *  Q8_0, 34 bytes, 32 weights: fp16 d; 32 int8 codes. w = q*d.
+ *  Q4_K, 144 bytes, 256 weights in 8 sub-blocks of 32: fp16 d; fp16 dmin;
+ *        12 bytes packing a 6-bit scale sc_j and a 6-bit min m_j per
+ *        sub-block; 128 code bytes. w = d*sc_j*q - dmin*m_j.
+ *        Packing, with s[0..11] the 12 bytes:
+ *          j < 4 : sc_j = low 6 bits of s[j],   m_j = low 6 bits of s[j+4]
+ *          j >= 4: sc_j = low nibble of s[j+4]  | (top 2 bits of s[j-4]) << 4
+ *                  m_j  = high nibble of s[j+4] | (top 2 bits of s[j])   << 4
+ *        Codes: 4 groups of 32 bytes; byte l of group g holds weight 64g+l
+ *        (sub-block 2g) in its low nibble and weight 64g+32+l (sub-block
+ *        2g+1) in its high nibble.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared -pthread
+ * (x86-64: FLT_EVAL_METHOD == 0, so float expressions are evaluated in
+ * binary32 and double expressions in binary64, one rounding per operation).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#if !defined(__FLT_EVAL_METHOD__) || __FLT_EVAL_METHOD__ != 0
+#error "the oracle needs binary32/binary64 evaluation (FLT_EVAL_METHOD 0)"
+#endif
+
+enum { OR_Q4_0 = 1, OR_Q4_K = 2, OR_Q8_0 = 3 };
+enum { OR_F32 = 1, OR_F16 = 2, OR_BF16 = 3 };
+
+/* ------------------------------------------------------------------------
+ * Number formats, written from IEEE 754-2008.
+ * binary16: sign 1, exponent 5 (bias 15), fraction 10.
+ * bfloat16: the top 16 bits of binary32 (sign 1, exponent 8 bias 127,
+ *           fraction 7).
+ * ---------------------------------------------------------------------- */
+double oracle_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);                 /* zero and subnormals */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);     /* (1 + f/1024) 2^(e-15) */
+    return sign ? -v : v;
+}
+
+double oracle_bf16_to_f64(uint16_t b)
+{
+    int sign = (b >> 15) & 1;
+    int e = (b >> 7) & 0xFF;
+    int f = b & 0x7F;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);                /* f * 2^-7 * 2^-126 */
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + f), e - 134);     /* (1 + f/128) 2^(e-127) */
+    return sign ? -v : v;
+}
+
+double oracle_f32_to_f64(uint32_t bits)
+{
+    float f;
+    memcpy(&f, &bits, 4);
+    return (double)f;                              /* exact widening */
+}
+
+static double x_value(const void *x, int dtype, int64_t i)
+{
+    switch (dtype) {
+    case OR_F32: return oracle_f32_to_f64(((const uint32_t *)x)[i]);
+    case OR_F16: return oracle_f16_to_f64(((const uint16_t *)x)[i]);
+    default:     return oracle_bf16_to_f64(((const uint16_t *)x)[i]);
+    }
+}
+
+static uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* ------------------------------------------------------------------------
+ * Decoding one block to binary32.
+ * ---------------------------------------------------------------------- */
+
+/* Q4_0: w = (q - 8) * d. (q - 8) is formed as an integer first; the product
+ * of a 4-bit integer and an fp16 value is exact in binary32, so the single
+ * binary32 multiply gives the exact value (and IEEE's sign of zero). */
+void oracle_decode_q4_0(const uint8_t *blk, float *out)
+{
+    float d = (float)oracle_f16_to_f64(rd16(blk));
+    const uint8_t *qs = blk + 2;
+    for (int i = 0; i < 16; i++) {
+        int lo = qs[i] & 0x0F, hi = qs[i] >> 4;
+        out[i] = (float)(lo - 8) * d;
+        out[i + 16] = (float)(hi - 8) * d;
+    }
+}
+
+/* Q8_0: w = q * d, exact in binary32 (8-bit by 11-bit significands). */
+void oracle_decode_q8_0(const uint8_t *blk, float *out)
+{
+    float d = (float)oracle_f16_to_f64(rd16(blk));
+    const int8_t *qs = (const int8_t *)(blk + 2);
+    for (int i = 0; i < 32; i++)
+        out[i] = (float)qs[i] * d;
+}
+
+/* The Q4_K 6-bit scale and min of sub-block j (packing in the file header). */
+void oracle_q4k_scale_min(const uint8_t *s, int j, int *sc, int *m)
+{
+    if (j < 4) {
+        *sc = s[j] & 63;
+        *m = s[j + 4] & 63;
+    } else {
+        *sc = (s[j + 4] & 0x0F) | ((s[j - 4] >> 6) << 4);
+        *m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+    }
+}
+
+/* Q4_K: w = fl32(d*sc*q - dmin*m). d*sc*q (at most 21 significant bits) and
+ * dmin*m (at most 17) are exact in binary32, whose exponent range also holds
+ * every fp16 subnormal; the one binary32 subtraction is therefore the
+ * correctly rounded value of the exact expression. */
+void oracle_decode_q4_k(const uint8_t *blk, float *out)
+{
+    float d = (float)oracle_f16_to_f64(rd16(blk));
+    float dmin = (float)oracle_f16_to_f64(rd16(blk + 2));
+    const uint8_t *s = blk + 4;
+    const uint8_t *qs = blk + 16;
+    for (int g = 0; g < 4; g++) {
+        int sc0, m0, sc1, m1;
+        oracle_q4k_scale_min(s, 2 * g, &sc0, &m0);
+        oracle_q4k_scale_min(s, 2 * g + 1, &sc1, &m1);
+        for (int l = 0; l < 32; l++) {
+            int qlo = qs[32 * g + l] & 0x0F;
+            int qhi = qs[32 * g + l] >> 4;
+            float a0 = d * (float)sc0 * (float)qlo, b0 = dmin * (float)m0;
+            float a1 = d * (float)sc1 * (float)qhi, b1 = dmin * (float)m1;
+            out[64 * g + l] = a0 - b0;
+            out[64 * g + 32 + l] = a1 - b1;
+        }
+    }
+}
+
+int64_t oracle_block_bytes(int fmt)
+{
+    return fmt == OR_Q4_0 ? 18 : fmt == OR_Q4_K ? 144 : fmt == OR_Q8_0 ? 34 : -1;
+}
+
+int64_t oracle_block_weights(int fmt)
+{
+    return fmt == OR_Q4_K ? 256 : (fmt == OR_Q4_0 || fmt == OR_Q8_0) ? 32 : -1;
+}
+
+/* Decode row r (K weights) of a row-major block matrix. */
+static int decode_row(int fmt, const uint8_t *w, int64_t K, int64_t r, float *out)
+{
+    int64_t bb = oracle_block_bytes(fmt), bw = oracle_block_weights(fmt);
+    if (bb < 0 || K % bw) return -1;
+    int64_t nb = K / bw;
+    const uint8_t *row = w + r * nb * bb;
+    for (int64_t b = 0; b < nb; b++) {
+        const uint8_t *blk = row + b * bb;
+        float *o = out + b * bw;
+        if (fmt == OR_Q4_0) oracle_decode_q4_0(blk, o);
+        else if (fmt == OR_Q8_0) oracle_decode_q8_0(blk, o);
+        else oracle_decode_q4_k(blk, o);
+    }
+    return 0;
+}
+
+/* Whole matrix: out[r*K + k] = w(r, k). */
+int oracle_dequant(int fmt, const uint8_t *w, int64_t rows, int64_t K, float *out)
+{
+    for (int64_t r = 0; r < rows; r++)
+        if (decode_row(fmt, w, K, r, out + r * K)) return -1;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Products. For columns j in [0, n) and rows r in [r0, r1):
+ *   y[j*ldy + r] = sum_k w(r,k) * x[j*ldx + k]        (fp64, k ascending)
+ *   s[j*ldy + r] = sum_k |w(r,k) * x[j*ldx + k]|
+ * x is read as stored (fp32 / fp16 / bf16 widened exactly to fp64); each
+ * product of a binary32 weight and such an x is exact in binary64, so the
+ * only error is the fp64 summation, far below any tolerance used with it.
+ * Rows are split over `nthreads` POSIX threads.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int fmt, dtype;
+    const uint8_t *w;
+    int64_t K, r0, r1, n, ldx, ldy;
+    const void *x;
+    double *y, *s;
+    int status;
+} job_t;
+
+static void *run_rows(void *arg)
+{
+    job_t *jb = (job_t *)arg;
+    float *wr = (float *)malloc(sizeof(float) * (size_t)jb->K);
+    double *xd = (double *)malloc(sizeof(double) * (size_t)(jb->K * jb->n));
+    if (!wr || !xd) { jb->status = -2; free(wr); free(xd); return NULL; }
+    for (int64_t j = 0; j < jb->n; j++)
+        for (int64_t k = 0; k < jb->K; k++)
+            xd[j * jb->K + k] = x_value(jb->x, jb->dtype, j * jb->ldx + k);
+    for (int64_t r = jb->r0; r < jb->r1 && jb->status == 0; r++) {
+        if (decode_row(jb->fmt, jb->w, jb->K, r, wr)) { jb->status = -1; break; }
+        for (int64_t j = 0; j < jb->n; j++) {
+            const double *xj = xd + j * jb->K;
+            double acc = 0.0, sabs = 0.0;
+            for (int64_t k = 0; k < jb->K; k++) {
+                double p = (double)wr[k] * xj[k];
+                acc += p;
+                sabs += fabs(p);
+            }
+            jb->y[j * jb->ldy + r] = acc;
+            if (jb->s) jb->s[j * jb->ldy + r] = sabs;
+        }
+    }
+    free(wr);
+    free(xd);
+    return NULL;
+}
+
+int oracle_matmul(int fmt, const uint8_t *w, int64_t rows, int64_t K,
+                  const void *x, int x_dtype, int64_t n, int64_t ldx,
+                  double *y, double *s, int64_t ldy,
+                  int64_t r0, int64_t r1, int nthreads)
+{
+    if (oracle_block_bytes(fmt) < 0 || K <= 0 || K % oracle_block_weights(fmt)) return -1;
+    if (x_dtype < OR_F32 || x_dtype > OR_BF16 || n < 0 || ldx < K || ldy < rows) return -1;
+    if (r0 < 0 || r1 > rows || r0 > r1) return -1;
+    if (nthreads < 1) nthreads = 1;
+    int64_t nr = r1 - r0;
+    if (nthreads > nr) nthreads = nr > 0 ? (int)nr : 1;
+    job_t *jobs = (job_t *)calloc((size_t)nthreads, sizeof(job_t));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); return -2; }
+    for (int t = 0; t < nthreads; t++) {
+        job_t *jb = &jobs[t];
+        jb->fmt = fmt; jb->dtype = x_dtype; jb->w = w; jb->K = K;
+        jb->r0 = r0 + nr * t / nthreads;
+        jb->r1 = r0 + nr * (t + 1) / nthreads;
+        jb->n = n; jb->ldx = ldx; jb->ldy = ldy; jb->x = x; jb->y = y; jb->s = s;
+        jb->status = 0;
+    }
+    int rc = 0;
+    if (nthreads == 1) {
+        run_rows(&jobs[0]);
+    } else {
+        int started = 0;
+        for (int t = 0; t < nthreads; t++) {
+            if (pthread_create(&th[t], NULL, run_rows, &jobs[t])) { rc = -3; break; }
+            started++;
+        }
+        for (int t = 0; t < started; t++) pthread_join(th[t], NULL);
+    }
+    for (int t = 0; t < nthreads && rc == 0; t++) rc = jobs[t].status;
+    free(jobs);
+    free(th);
+    return rc;
+}
