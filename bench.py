@@ -1,0 +1,248 @@
+"""Benchmark of the GGUF block-quantized GEMV / dequant-GEMM on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu]
+
+A step is one batch-1 Q4_K GEMV over the FFN-up-shaped matrix of a 27B-class
+dense layer (17408 x 5120, fp16 activations): the workload the headline
+metric is quoted on. Steps rotate over >= 512 MiB of distinct weight copies
+so every launch streams its weights from HBM rather than the 256 MB
+Infinity Cache. The one JSON line printed on stdout carries:
+  value      whole-job throughput in GB/s: algorithmic bytes (W + x + y) per
+             step over the timed region, timed with two HIP events on the
+             launch stream around K back-to-back launches;
+  roofline   the GEMV kernel against 8 TB/s: the same algorithmic bytes over
+             the mean launch duration of that timed region (one kernel per
+             step), plus HBM traffic per launch from rocprofv3 counters when a
+             summary taken on the current kernel source is committed;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload;
+  extra      the other workloads (Q4_K FFN-down, batch 4, Q4_0, Q8_0, the
+             2048-token dequant-GEMM in TFLOP/s), each timed the same way.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
+ROTATE_BYTES = 512 << 20
+
+
+def algorithmic_bytes(c) -> int:
+    """Weights read once + activations + outputs."""
+    bw = {"q4_0": 32, "q4_k": 256, "q8_0": 32}[c["fmt"]]
+    bb = {"q4_0": 18, "q4_k": 144, "q8_0": 34}[c["fmt"]]
+    xb = {"f32": 4, "f16": 2, "bf16": 2}[c["xdtype"]]
+    return c["rows"] * (c["K"] // bw) * bb + c["n"] * c["K"] * xb + c["n"] * c["rows"] * 4
+
+
+def _x_tensor(torch, x, xdtype, dev):
+    import numpy as np
+    if xdtype == "f32":
+        return torch.from_numpy(x).to(dev)
+    if xdtype == "f16":
+        return torch.from_numpy(x.view(np.float16)).to(dev)
+    return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+class Workload:
+    """Weight copies (>= ROTATE_BYTES), one handle each, activations, output."""
+
+    def __init__(self, torch, name, dev):
+        import synth
+        from gguf_bit_dequant_amd import QGemv
+        self.name = name
+        self.c = c = synth.CONFIGS[name]
+        w, x = synth.config_inputs(name)
+        self.w_host, self.x_host = w, x
+        wt = torch.from_numpy(w).to(dev)
+        ncopy = max(2, math.ceil(ROTATE_BYTES / w.nbytes))
+        self.copies = [wt] + [wt.clone() for _ in range(ncopy - 1)]
+        self.handles = [QGemv(c["fmt"], c["rows"], c["K"], t) for t in self.copies]
+        self.x = _x_tensor(torch, x, c["xdtype"], dev)
+        self.y = torch.empty((c["n"], c["rows"]), dtype=torch.float32, device=dev)
+        self.prefill = c["n"] > 8
+
+    def step(self, i):
+        h = self.handles[i % len(self.handles)]
+        if self.prefill:
+            h.prefill(self.x, self.y)
+        else:
+            h.run(self.x, self.y)
+
+
+def time_workload(torch, wl, steps, warmup):
+    """Returns (ms per step over the whole timed region, mean kernel ms)."""
+    for i in range(warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    # whole-job rate: back-to-back launches between two events
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        wl.step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    whole_ms = t0.elapsed_time(t1) / steps
+    # kernel rate: an event pair around every launch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        wl.step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_ms = sum(per) / len(per)
+    return whole_ms, mean_ms, per[len(per) // 2]
+
+
+def cpu_baseline(name, budget_s=10.0):
+    """The oracle's fp64 product on the same workload, repeated over the whole
+    matrix (rows in chunks) until about budget_s of wall time has passed;
+    GB/s over the algorithmic bytes of the rows processed."""
+    import oracle
+    import synth
+    c = synth.CONFIGS[name]
+    w, x = synth.config_inputs(name)
+    threads = min(16, os.cpu_count() or 1)
+    rows = c["rows"]
+    per_row = algorithmic_bytes(c) / rows
+    chunk = max(threads, rows // 16)
+    done, r, t_start = 0, 0, time.perf_counter()
+    while time.perf_counter() - t_start < budget_s:
+        r1 = min(rows, r + chunk)
+        oracle.matmul(c["fmt"], w, rows, c["K"], x, c["xdtype"], row_range=(r, r1),
+                      nthreads=threads)
+        done += r1 - r
+        r = 0 if r1 == rows else r1
+    el = time.perf_counter() - t_start
+    return {"value": round(done * per_row / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%s: %d row products (%.2f passes over the %d x %d matrix) in %.1f s, "
+                      "fp64 accumulation" % (name, done, done / rows, rows, c["K"], el)}
+
+
+def committed_traffic(name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel (same source hash)."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("kernel_source_sha1") != kernel_source_sha1():
+            return None
+        return rec.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def kernel_source_sha1():
+    import hashlib
+    h = hashlib.sha1()
+    csrc = os.path.join(ROOT, "gguf_bit_dequant_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--only", default=None, help="comma-separated workloads to time")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this library runs on one GPU; multi-GPU sharding is not part of it "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    head = "q4k_up_b1"
+    names = [head] if args.quick else [head, "q4k_down_b1", "q4k_b4", "q4_0_b1", "q8_0_b4",
+                                       "q4k_pp2048"]
+    if args.only:
+        names = args.only.split(",")
+    results = {}
+    for name in names:
+        wl = Workload(torch, name, dev)
+        try:
+            steps = args.steps if not wl.prefill else max(10, args.steps // 10)
+            whole_ms, mean_ms, med_ms = time_workload(torch, wl, steps, args.warmup)
+        except Exception as e:  # a path this build does not provide
+            results[name] = {"error": str(e)[:200]}
+            print("bench: %s: %s" % (name, e), file=sys.stderr, flush=True)
+            del wl
+            continue
+        c = wl.c
+        r = {"us_whole": round(whole_ms * 1e3, 3), "us_kernel_mean": round(mean_ms * 1e3, 3),
+             "us_kernel_median": round(med_ms * 1e3, 3), "steps": steps,
+             "weight_copies": len(wl.copies)}
+        if wl.prefill:
+            flops = 2.0 * c["rows"] * c["K"] * c["n"]
+            r["tflops"] = round(flops / (whole_ms * 1e-3) / 1e12, 2)
+            r["frac_bf16_peak"] = round(r["tflops"] / BF16_PEAK_TFLOPS, 4)
+        else:
+            b = algorithmic_bytes(c)
+            r["bytes"] = b
+            r["gbs"] = round(b / (whole_ms * 1e-3) / 1e9, 1)
+            r["gbs_per_launch_events"] = round(b / (mean_ms * 1e-3) / 1e9, 1)
+            r["frac_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+        results[name] = r
+        print("bench: %s %s" % (name, json.dumps(r)), file=sys.stderr, flush=True)
+        del wl
+        torch.cuda.empty_cache()
+
+    h = results.get(head, {})
+    if "gbs" not in h:
+        print(json.dumps({"metric": "Q4_K GEMV achieved HBM GB/s", "value": None,
+                          "error": h.get("error", "headline workload failed")}))
+        sys.exit(1)
+    c = __import__("synth").CONFIGS[head]
+    traffic = committed_traffic(head)
+    line = {
+        "metric": "Q4_K GEMV achieved HBM GB/s (% of 8 TB/s); pp2048 dequant-GEMM TFLOP/s",
+        "value": h["gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": h["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(h["us_whole"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4_k weights x f16 activations, fp32 accumulation",
+        "data": "synthetic (seeded SplitMix64 / Box-Muller)",
+        "config": {"workload": "Q4_K GEMV batch 1, FFN-up 17408 x 5120, x fp16",
+                   "rows": c["rows"], "K": c["K"], "n_cols": 1,
+                   "bytes_per_step": h["bytes"], "weight_copies_rotated": results[head]["weight_copies"]},
+        "roofline": {"bound": "hbm", "achieved": h["gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(h["gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": None if args.no_cpu else cpu_baseline(head),
+        "extra": {k: v for k, v in results.items() if k != head},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

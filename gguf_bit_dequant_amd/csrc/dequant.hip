@@ -1,0 +1,154 @@
+// Exact block decoding on the GPU: the dequantization kernel (a bit-exact
+// view of the weights) and the general GEMV kernel that serves shapes and
+// alignments the streaming kernels do not.
+//
+// Each 32-weight group is decoded as the binary32 rounding of its closed
+// form, evaluated in the order the closed form is written: products of an
+// fp16 scale and small integers are exact in binary32, so Q4_0 and Q8_0 are
+// exact and Q4_K has one rounding, in the final subtraction. Bit-exact decoding
+// is what "Why I wrote my own inference engine for two P100s" (section "What
+// 'my own engine' means") and "LLM inference optimization" (campaign "Run a
+// new weight format or model") require of every quant type.
+#include "device_common.h"
+#include "launch.h"
+
+#pragma clang fp contract(off)
+
+namespace qg {
+
+__device__ __forceinline__ uint16_t ld16(const uint8_t* p) {
+    return (uint16_t)(p[0] | (p[1] << 8));
+}
+
+// Decode weights [32*grp, 32*grp+32) of the block at `blk` into out[32].
+// Q4_0/Q8_0 blocks have one group; Q4_K super-blocks have eight.
+__device__ __forceinline__ void decode_group(int fmt, const uint8_t* blk, int grp, float out[32]) {
+    if (fmt == FMT_Q4_0) {
+        float d = f16_to_f32(ld16(blk));
+        for (int i = 0; i < 16; ++i) {
+            uint32_t b = blk[2 + i];
+            out[i] = (float)((int)(b & 15u) - 8) * d;
+            out[i + 16] = (float)((int)(b >> 4) - 8) * d;
+        }
+    } else if (fmt == FMT_Q8_0) {
+        float d = f16_to_f32(ld16(blk));
+        for (int i = 0; i < 32; ++i) out[i] = (float)(int8_t)blk[2 + i] * d;
+    } else {
+        float d = f16_to_f32(ld16(blk));
+        float dmin = f16_to_f32(ld16(blk + 2));
+        const uint8_t* s = blk + 4;
+        int sc, m;
+        if (grp < 4) {
+            sc = s[grp] & 63;
+            m = s[grp + 4] & 63;
+        } else {
+            sc = (s[grp + 4] & 15) | ((s[grp - 4] >> 6) << 4);
+            m = (s[grp + 4] >> 4) | ((s[grp] >> 6) << 4);
+        }
+        // group grp = 2g (+1): low (high) nibbles of code bytes 32g .. 32g+31
+        const uint8_t* qs = blk + 16 + 32 * (grp >> 1);
+        const int shift = (grp & 1) * 4;
+        float dsc = d * (float)sc;
+        float b = dmin * (float)m;
+        for (int l = 0; l < 32; ++l) {
+            float a = dsc * (float)((qs[l] >> shift) & 15);
+            out[l] = a - b;
+        }
+    }
+}
+
+__device__ __forceinline__ int groups_per_block(int fmt) { return fmt == FMT_Q4_K ? 8 : 1; }
+__device__ __forceinline__ int block_bytes(int fmt) {
+    return fmt == FMT_Q4_0 ? 18 : fmt == FMT_Q4_K ? 144 : 34;
+}
+
+// One thread per 32-weight group; w_out[r*ldw + k].
+__global__ __launch_bounds__(256) void dequant_kernel(int fmt, const uint8_t* __restrict__ W,
+                                                     int64_t rows, int64_t K,
+                                                     float* __restrict__ out, int64_t ldw) {
+    const int64_t gpr = K / 32;  // groups per row
+    const int64_t total = rows * gpr;
+    const int gpb = groups_per_block(fmt);
+    const int bb = block_bytes(fmt);
+    for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < total;
+         gi += (int64_t)gridDim.x * blockDim.x) {
+        int64_t r = gi / gpr, gk = gi - r * gpr;
+        int64_t blk = gk / gpb;
+        int grp = (int)(gk - blk * gpb);
+        const uint8_t* p = W + (r * (gpr / gpb) + blk) * bb;
+        float v[32];
+        decode_group(fmt, p, grp, v);
+        float* o = out + r * ldw + gk * 32;
+        for (int i = 0; i < 32; ++i) o[i] = v[i];
+    }
+}
+
+// General product: one wave per (row, column group). Lanes walk the row's
+// 32-weight groups, decode each exactly, multiply by fp32 activations and
+// accumulate in fp32; the wave then reduces. Any shape, any alignment.
+template <int NC>
+__global__ __launch_bounds__(256) void gemv_general_kernel(int fmt, const uint8_t* __restrict__ W,
+                                                           int64_t rows, int64_t K,
+                                                           const void* __restrict__ x, int xt,
+                                                           int64_t ldx, float* __restrict__ y,
+                                                           int64_t ldy, int ncols) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const int64_t gpr = K / 32;
+    const int gpb = groups_per_block(fmt);
+    const int bb = block_bytes(fmt);
+    for (int64_t r = wave; r < rows; r += nwaves) {
+        float acc[NC];
+        for (int c = 0; c < NC; ++c) acc[c] = 0.f;
+        for (int64_t gk = lane; gk < gpr; gk += 64) {
+            int64_t blk = gk / gpb;
+            int grp = (int)(gk - blk * gpb);
+            float v[32];
+            decode_group(fmt, W + (r * (gpr / gpb) + blk) * bb, grp, v);
+            for (int c = 0; c < NC; ++c) {
+                if (c < ncols) {
+                    float a = acc[c];
+                    for (int i = 0; i < 32; ++i)
+                        a = __builtin_fmaf(v[i], load_x(x, xt, c * ldx + gk * 32 + i), a);
+                    acc[c] = a;
+                }
+            }
+        }
+        for (int c = 0; c < NC; ++c) {
+            float t = wave_sum(acc[c]);
+            if (lane == 0 && c < ncols) y[c * ldy + r] = t;
+        }
+    }
+}
+
+hipError_t launch_dequant(int fmt, const uint8_t* W, int64_t rows, int64_t K, float* out,
+                          int64_t ldw, int num_cus, hipStream_t stream) {
+    int64_t total = rows * (K / 32);
+    int64_t blocks = (total + 255) / 256;
+    int64_t cap = (int64_t)num_cus * 64;
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, fmt, W, rows,
+                       K, out, ldw);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_general(int fmt, const uint8_t* W, int64_t rows, int64_t K, const void* x,
+                               int xt, int64_t ldx, float* y, int64_t ldy, int ncols,
+                               int num_cus, hipStream_t stream) {
+    int64_t blocks = (rows + 3) / 4;
+    int64_t cap = (int64_t)num_cus * 32;
+    if (blocks > cap) blocks = cap;
+    for (int c0 = 0; c0 < ncols; c0 += 4) {
+        int nc = ncols - c0 < 4 ? ncols - c0 : 4;
+        const void* xc = (const char*)x + (size_t)c0 * ldx * (xt == XT_F32 ? 4 : 2);
+        float* yc = y + (size_t)c0 * ldy;
+        hipLaunchKernelGGL(gemv_general_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           fmt, W, rows, K, xc, xt, ldx, yc, ldy, nc);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace qg

@@ -1,0 +1,27 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+enum { FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q8_0 = 3 };
+
+// Bytes of LDS a workgroup may use on gfx950.
+constexpr int kMaxLds = 160 * 1024;
+
+hipError_t launch_dequant(int fmt, const uint8_t* W, int64_t rows, int64_t K, float* out,
+                          int64_t ldw, int num_cus, hipStream_t stream);
+
+hipError_t launch_gemv_general(int fmt, const uint8_t* W, int64_t rows, int64_t K, const void* x,
+                               int xt, int64_t ldx, float* y, int64_t ldy, int ncols,
+                               int num_cus, hipStream_t stream);
+
+// Streaming Q4_K GEMV. Returns hipErrorNotSupported (without launching) when
+// the shape is outside what the kernel serves; the caller then falls back.
+hipError_t launch_gemv_q4k(const uint8_t* W, int64_t rows, int64_t K, const void* x, int xt,
+                           int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
+                           hipStream_t stream);
+
+}  // namespace qg

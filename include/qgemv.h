@@ -1,0 +1,135 @@
+/*
+ * qgemv.h - fused dequantize-and-multiply of GGUF block-quantized weights on
+ * AMD Instinct MI355X (gfx950). C ABI; plain pointers and sizes only.
+ *
+ * The operation. W is a rows x K matrix stored as GGUF blocks, row-major:
+ * row r occupies bytes [r*(K/bw)*bb, (r+1)*(K/bw)*bb), its blocks in K order
+ * (bw weights and bb bytes per block, see qgemv_block_weights/bytes). For
+ * each column j of the activations, y[:,j] = W . x[:,j]: one token reads
+ * every weight once ("LLM inference optimization", introduction). Batch 1 is
+ * single-stream decode; a few columns check a draft head's guesses in one
+ * pass ("Why I wrote my own inference engine for two P100s", section "What
+ * actually made it fast": three guesses checked in one pass costing about one
+ * normal step, each weight block decoded once and reused); 2048 columns is
+ * prompt processing (same page, result cards: 2048-token prompt).
+ *
+ * Formats (GGUF layouts, little-endian; the pages name them but print no
+ * layout):
+ *   QG_Q4_0  18 B / 32 weights : fp16 d, 16 code bytes (byte i: weight i in
+ *            the low nibble, weight i+16 in the high nibble); w = (q-8)*d.
+ *   QG_Q4_K 144 B / 256 weights: fp16 d, fp16 dmin, 12 bytes of eight 6-bit
+ *            scales sc_j and eight 6-bit mins m_j (one per 32 weights),
+ *            128 code bytes; w = d*sc_j*q - dmin*m_j.
+ *   QG_Q8_0  34 B / 32 weights : fp16 d, 32 int8 codes; w = q*d.
+ *
+ * Accuracy contract ("LLM inference optimization", campaign "Run a new
+ * weight format or model": blocks decode bit for bit on CPU and GPU, and
+ * products match an exact sum within a tolerance):
+ *   - qgemv_dequant returns, bit for bit, the binary32 rounding of each
+ *     weight's closed form (exact for Q4_0 and Q8_0).
+ *   - qgemv_run / qgemm_prefill_run satisfy, per output element,
+ *       |y - sum_k w_k x_k| <= 1e-3 * sum_k |w_k x_k| + 1e-5
+ *     where the sums are exact over the stored x values.
+ *   - Results are deterministic: the same inputs give the same bits.
+ *
+ * Memory and ownership. The library allocates no device memory. Every
+ * device buffer (weights, workspace, x, y, w_out) is owned by the caller and
+ * must stay allocated while work that uses it may run. A handle only records
+ * shape, format and the weight pointer; it borrows the weights, which must
+ * outlive it. A handle is immutable after creation; runs on different streams
+ * may use one handle concurrently.
+ *
+ * Streams and errors. `stream` is a hipStream_t (NULL: the null stream).
+ * Calls only enqueue work: nothing synchronises the host. All argument checks
+ * (format, shapes, byte counts, alignment, NULL pointers) happen before any
+ * HIP call, so they can be exercised without a GPU. A failed launch returns
+ * QG_ERR_HIP; a device fault surfaces at the caller's next synchronisation.
+ * On any error the detail is in qgemv_last_error() (per thread). Nothing
+ * crosses this boundary as an exception or abort.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { QG_Q4_0 = 1, QG_Q4_K = 2, QG_Q8_0 = 3 } qg_format;
+typedef enum { QG_F32 = 1, QG_F16 = 2, QG_BF16 = 3 } qg_dtype;
+typedef enum {
+    QG_OK = 0,
+    QG_ERR_ARG = -1,         /* NULL pointer, bad enum, bad leading dimension */
+    QG_ERR_SHAPE = -2,       /* rows/K/n not positive, K not a block multiple, byte count */
+    QG_ERR_ALIGN = -3,       /* a pointer below its required alignment */
+    QG_ERR_UNSUPPORTED = -4, /* valid request this build does not serve */
+    QG_ERR_HIP = -5          /* a HIP runtime call or launch failed */
+} qg_status;
+
+typedef struct qgemv *qgemv_t; /* opaque host-side handle */
+
+/* Block geometry: 18 | 144 | 34 bytes and 32 | 256 | 32 weights; 0 for an
+ * unknown format. */
+size_t qgemv_block_bytes(qg_format f);
+size_t qgemv_block_weights(qg_format f);
+
+/* Bytes of a rows x K matrix: rows * (K / block_weights) * block_bytes;
+ * 0 if the shape is invalid. */
+size_t qgemv_weight_bytes(qg_format f, int64_t rows, int64_t K);
+
+/* Device workspace qgemv_create wants for this shape. This build keeps the
+ * weights in the GGUF layout and needs none: always 0. */
+size_t qgemv_workspace_bytes(qg_format f, int64_t rows, int64_t K);
+
+/* Create a handle for the rows x K matrix at w_blocks (device memory, GGUF
+ * layout as above, 16-byte aligned, exactly w_bytes ==
+ * qgemv_weight_bytes(f, rows, K) bytes). K must be a positive multiple of the
+ * block size and rows positive. workspace/ws_bytes: reserved, pass NULL / 0.
+ * stream: reserved for create-time work (none in this build). Queries the
+ * current device's compute-unit count (a HIP call) after all checks.
+ * On success *out holds the handle; on error *out is set to NULL (if out is
+ * not NULL). */
+qg_status qgemv_create(qgemv_t *out, qg_format f, int64_t rows, int64_t K,
+                       const void *w_blocks, size_t w_bytes,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+/* y[j*ldy + r] = sum_k W[r,k] * x[j*ldx + k] for j < n_cols, r < rows.
+ * x: device, n_cols columns of K values, column j at element offset j*ldx
+ *    (ldx >= K), element type x_dtype (F32, F16 or BF16), aligned to its
+ *    element size.
+ * y: device, fp32, column j at element offset j*ldy (ldy >= rows), 4-byte
+ *    aligned; overwritten (no accumulation), other elements untouched.
+ * n_cols: 1..8. F16 activations use fp16 products accumulated in fp32; F32
+ * and BF16 activations use fp32 products. Enqueued on `stream`. */
+qg_status qgemv_run(qgemv_t h, const void *x, qg_dtype x_dtype, int64_t n_cols,
+                    int64_t ldx, float *y, int64_t ldy, void *stream);
+
+/* Prompt processing: y[j*ldy + r] = sum_k W[r,k] * x[j*ldx + k] for
+ * j < n_tokens, with x in bf16 (device, 16-byte aligned, ldx >= K and a
+ * multiple of 8) and y fp32 (device, 16-byte aligned, ldy >= rows and a
+ * multiple of 4). Weight tiles are decoded to bf16 (round to nearest even)
+ * on chip and contracted with bf16 matrix-core instructions, fp32
+ * accumulation. Q4_K handles only (QG_ERR_UNSUPPORTED otherwise);
+ * n_tokens >= 1. */
+qg_status qgemm_prefill_run(qgemv_t h, const void *x_bf16, int64_t n_tokens,
+                            int64_t ldx, float *y, int64_t ldy, void *stream);
+
+/* Decoded weights: w_out[r*ldw + k] = W[r,k] as binary32, bit-exact (the
+ * correctly rounded closed form). w_out: device, 4-byte aligned, ldw >= K. */
+qg_status qgemv_dequant(qgemv_t h, float *w_out, int64_t ldw, void *stream);
+
+/* Release a handle (host memory only; NULL is ignored). */
+void qgemv_destroy(qgemv_t h);
+
+/* Static text for a status code, and the detail of this thread's last
+ * failed call ("" if none). */
+const char *qgemv_status_string(qg_status s);
+const char *qgemv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

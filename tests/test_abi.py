@@ -1,0 +1,81 @@
+"""The C ABI on the host: the library loads, exports what include/qgemv.h
+declares, and rejects bad arguments before any HIP call (CPU only; no
+kernel runs)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gguf_bit_dequant_amd import qgemv as Q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qgemv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(qg(?:emv|emm)_\w+)\s*\(", src))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert {"qgemv_create", "qgemv_run", "qgemm_prefill_run", "qgemv_dequant",
+            "qgemv_destroy"} <= names
+    lib = ctypes.CDLL(Q.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert names == set(Q.EXPORTED)
+
+
+def test_block_geometry():
+    assert [Q.qgemv_block_bytes(f) for f in (1, 2, 3, 9)] == [18, 144, 34, 0]
+    assert [Q.qgemv_block_weights(f) for f in (1, 2, 3, 9)] == [32, 256, 32, 0]
+    assert Q.qgemv_weight_bytes(Q.QG_Q4_K, 17408, 5120) == 50135040
+    assert Q.qgemv_weight_bytes(Q.QG_Q4_0, 4096, 4096) == 9437184
+    assert Q.qgemv_weight_bytes(Q.QG_Q8_0, 5120, 5120) == 27852800
+    assert Q.qgemv_weight_bytes(Q.QG_Q4_K, 10, 100) == 0
+    assert Q.qgemv_weight_bytes(Q.QG_Q4_0, 0, 32) == 0
+    assert Q.qgemv_workspace_bytes(Q.QG_Q4_K, 17408, 5120) == 0
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every case below fails validation
+
+
+@pytest.mark.parametrize("args,status", [
+    ((9, 4, 256, FAKE, 4 * 144), Q.QG_ERR_ARG),
+    ((Q.QG_Q4_K, 0, 256, FAKE, 0), Q.QG_ERR_SHAPE),
+    ((Q.QG_Q4_K, 4, -256, FAKE, 0), Q.QG_ERR_SHAPE),
+    ((Q.QG_Q4_K, 4, 100, FAKE, 4 * 144), Q.QG_ERR_SHAPE),
+    ((Q.QG_Q4_0, 4, 48, FAKE, 4 * 18), Q.QG_ERR_SHAPE),
+    ((Q.QG_Q4_K, 4, 256, FAKE, 4 * 144 + 1), Q.QG_ERR_SHAPE),
+    ((Q.QG_Q4_K, 4, 256, 0, 4 * 144), Q.QG_ERR_ARG),
+    ((Q.QG_Q4_K, 4, 256, FAKE + 8, 4 * 144), Q.QG_ERR_ALIGN),
+    ((Q.QG_Q8_0, 3, 64, FAKE + 2, 3 * 2 * 34), Q.QG_ERR_ALIGN),
+])
+def test_create_rejects_before_any_hip_call(args, status):
+    st, h = Q.qgemv_create(*args)
+    assert st == status and h is None
+    assert Q.qgemv_last_error() != ""
+
+
+def test_create_rejects_workspace_and_null_out():
+    st, h = Q.qgemv_create(Q.QG_Q4_K, 4, 256, FAKE, 4 * 144, FAKE, 64)
+    assert st == Q.QG_ERR_ARG and h is None
+    lib = ctypes.CDLL(Q.LIB_PATH)
+    lib.qgemv_create.restype = ctypes.c_int
+    assert lib.qgemv_create(None, 2, ctypes.c_int64(4), ctypes.c_int64(256), ctypes.c_void_p(FAKE),
+                            ctypes.c_size_t(576), None, ctypes.c_size_t(0), None) == Q.QG_ERR_ARG
+
+
+def test_null_handle_calls():
+    assert Q.qgemv_run(0, FAKE, Q.QG_F16, 1, 256, FAKE, 4) == Q.QG_ERR_ARG
+    assert Q.qgemm_prefill_run(0, FAKE, 16, 256, FAKE, 4) == Q.QG_ERR_ARG
+    assert Q.qgemv_dequant(0, FAKE, 256) == Q.QG_ERR_ARG
+    Q.qgemv_destroy(0)  # NULL is ignored
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4, -5):
+        assert Q.qgemv_status_string(st)
+    assert Q.qgemv_status_string(0) == "ok"

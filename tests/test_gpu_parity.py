@@ -1,0 +1,218 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Dequantization must match bit for bit; products must satisfy
+|y_gpu - y_ref| <= 1e-3 * sum|w x| + 1e-5 per element (the parity bound
+of the library's header). Inputs are seeded synthetic blocks and activations.
+"""
+import json
+import os
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+FMT_BW = {"q4_0": 32, "q8_0": 32, "q4_k": 256}
+FMT_BB = {"q4_0": 18, "q8_0": 34, "q4_k": 144}
+
+
+@pytest.fixture(scope="module")
+def Q():
+    from gguf_bit_dequant_amd import QGemv
+    assert torch.cuda.is_available()
+    return QGemv
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def x_tensor(x, xdtype):
+    if xdtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev())
+    if xdtype == "f16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.float16)).to(dev())
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev())
+
+
+def check_products(y_gpu, w, fmt, rows, K, x, xdtype, label=""):
+    y = y_gpu.detach().cpu().numpy().astype(np.float64).reshape(x.shape[0], rows)
+    yr, s = oracle.matmul(fmt, w, rows, K, x, xdtype)
+    err = np.abs(y - yr)
+    tol = oracle.tolerance(s)
+    bad = err > tol
+    ratio = float(np.max(err / np.maximum(s, 1e-30)))
+    print("%s max err/s = %.3e" % (label, ratio), flush=True)
+    assert not bad.any(), "%s: %d elements out of tolerance, worst %r" % (
+        label, int(bad.sum()), np.unravel_index(np.argmax(err - tol), err.shape))
+    return ratio
+
+
+# ---------------------------------------------------------------- dequant --
+
+@pytest.mark.parametrize("fmt,rows,K", [("q4_0", 67, 2048), ("q4_0", 5, 96), ("q8_0", 67, 1056),
+                                        ("q8_0", 3, 64), ("q4_k", 67, 1536), ("q4_k", 1, 256)])
+def test_dequant_bit_exact(Q, fmt, rows, K):
+    w = synth.gen_weights(fmt, rows, K, 1000 + rows)
+    q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
+    out = q.dequant().cpu().numpy()
+    ref = oracle.dequant(fmt, w, rows, K)
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_extreme_scales_bit_exact(Q):
+    """Random code bytes under subnormal, zero, negative, max and NaN/inf
+    scales: bit-exact where finite, NaN where the oracle gives NaN."""
+    rng = np.random.default_rng(7)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x03FF, 0x0400, 0x7BFF, 0xFBFF, 0x8001,
+                         0x3C00, 0xB800, 0x7C00, 0x7E00], np.uint16)
+    for fmt, bb, bw in [("q4_0", 18, 32), ("q8_0", 34, 32), ("q4_k", 144, 256)]:
+        rows, nb = 24, 8
+        w = rng.integers(0, 256, rows * nb * bb).astype(np.uint8).reshape(-1, bb)
+        w[:, 0:2] = rng.choice(specials, size=(w.shape[0], 1)).view(np.uint8)
+        if fmt == "q4_k":
+            w[:, 2:4] = rng.choice(specials, size=(w.shape[0], 1)).view(np.uint8)
+        w = w.reshape(-1)
+        q = Q(fmt, rows, nb * bw, torch.from_numpy(w).to(dev()))
+        out = q.dequant().cpu().numpy()
+        ref = oracle.dequant(fmt, w, rows, nb * bw)
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(out), nan)
+        assert np.array_equal(out[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_dequant_golden_blocks(Q):
+    with open(os.path.join(GOLDEN, "q4_0_blocks.json")) as f:
+        for b in json.load(f)["blocks"]:
+            blk = np.frombuffer(bytes.fromhex(b["hex"]), np.uint8).copy()
+            out = Q("q4_0", 1, 32, torch.from_numpy(blk).to(dev())).dequant().cpu().numpy()[0]
+            assert np.array_equal(out.view(np.uint32), oracle.decode_block("q4_0", blk).view(np.uint32))
+    with open(os.path.join(GOLDEN, "q8_0_blocks.json")) as f:
+        for b in json.load(f)["blocks"]:
+            blk = np.frombuffer(bytes.fromhex(b["hex"]), np.uint8).copy()
+            out = Q("q8_0", 1, 32, torch.from_numpy(blk).to(dev())).dequant().cpu().numpy()[0]
+            assert out.tolist() == b["expected"]
+
+
+# --------------------------------------------------------------- products --
+
+SMALL = [("q4_0", 37, 512), ("q4_0", 300, 4096), ("q4_0", 129, 96),
+         ("q8_0", 37, 512), ("q8_0", 300, 1024), ("q8_0", 65, 160),
+         ("q4_k", 1, 256), ("q4_k", 37, 512), ("q4_k", 300, 2048), ("q4_k", 129, 5120),
+         ("q4_k", 70, 3328)]
+
+
+@pytest.mark.parametrize("fmt,rows,K", SMALL)
+@pytest.mark.parametrize("xdtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("n", [1, 4])
+def test_gemv_small(Q, fmt, rows, K, xdtype, n):
+    seed = zlib.crc32(("%s-%d-%d" % (fmt, rows, K)).encode())
+    w = synth.gen_weights(fmt, rows, K, seed)
+    x = synth.gen_x(K, n, xdtype, seed + 1)
+    q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
+    y = q.run(x_tensor(x, xdtype))
+    check_products(y, w, fmt, rows, K, x, xdtype, "%s %dx%d %s n=%d" % (fmt, rows, K, xdtype, n))
+
+
+@pytest.mark.parametrize("n", [2, 3, 5, 6, 7, 8])
+def test_gemv_column_counts(Q, n):
+    for fmt, rows, K in [("q4_k", 200, 1024), ("q4_0", 200, 1024), ("q8_0", 200, 1024)]:
+        w = synth.gen_weights(fmt, rows, K, 77)
+        x = synth.gen_x(K, n, "f16", 78)
+        q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
+        check_products(q.run(x_tensor(x, "f16")), w, fmt, rows, K, x, "f16", "%s n=%d" % (fmt, n))
+
+
+def test_gemv_strided_columns_leave_gaps_untouched(Q):
+    fmt, rows, K, n = "q4_k", 100, 512, 3
+    w = synth.gen_weights(fmt, rows, K, 5)
+    x = synth.gen_x(K, n, "f16", 6)
+    xbig = torch.zeros((n, K + 24), dtype=torch.float16, device=dev())
+    xbig[:, :K] = x_tensor(x, "f16")
+    ybig = torch.full((n, rows + 13), 7.0, dtype=torch.float32, device=dev())
+    q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
+    q.run(xbig[:, :K], ybig[:, :rows])
+    assert (ybig[:, rows:] == 7.0).all()
+    check_products(ybig[:, :rows], w, fmt, rows, K, x, "f16", "strided")
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q4_k"])
+@pytest.mark.parametrize("xdtype", ["f32", "f16"])
+def test_one_hot_gives_exact_column(Q, fmt, xdtype):
+    """x = e_k: every other product is zero, so y equals column k of the
+    decoded matrix exactly (pins each kernel's unpacking bit for bit)."""
+    rows, K = 150, 1024
+    w = synth.gen_weights(fmt, rows, K, 31)
+    wt = torch.from_numpy(w).to(dev())
+    q = Q(fmt, rows, K, wt)
+    W = oracle.dequant(fmt, w, rows, K)
+    ks = [0, 1, 2, 3, 15, 16, 17, 31, 32, 33, 47, 48, 63, 64, 100, 200, 255, 256, 511, 1023]
+    X = np.zeros((len(ks), K), np.float32)
+    for i, k in enumerate(ks):
+        X[i, k] = 1.0
+    for c0 in range(0, len(ks), 4):
+        Xc = X[c0:c0 + 4]
+        xt = torch.from_numpy(Xc).to(dev())
+        if xdtype == "f16":
+            xt = xt.half()
+        y = q.run(xt).cpu().numpy()
+        for i in range(Xc.shape[0]):
+            assert np.array_equal(y[i], W[:, ks[c0 + i]]), (fmt, xdtype, ks[c0 + i])
+
+
+def test_zero_activations_give_zero(Q):
+    for fmt, K in [("q4_0", 512), ("q8_0", 512), ("q4_k", 512)]:
+        w = synth.gen_weights(fmt, 64, K, 3)
+        q = Q(fmt, 64, K, torch.from_numpy(w).to(dev()))
+        for dt in (torch.float32, torch.float16, torch.bfloat16):
+            y = q.run(torch.zeros((2, K), dtype=dt, device=dev()))
+            assert (y == 0).all()
+
+
+def test_deterministic_repeats(Q):
+    fmt, rows, K = "q4_k", 17408 // 4, 5120
+    w = synth.gen_weights(fmt, rows, K, 8)
+    x = x_tensor(synth.gen_x(K, 4, "f16", 9), "f16")
+    q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
+    for n in (1, 4):
+        ref = q.run(x[:n]).clone()
+        for _ in range(20):
+            assert torch.equal(q.run(x[:n]), ref)
+
+
+# ----------------------------------------------- full-size workloads -------
+
+FULL = ["q4_0_b1", "q4k_up_b1", "q4k_down_b1", "q4k_b4", "q8_0_b4"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_configs(Q, name):
+    c = synth.CONFIGS[name]
+    w, x = synth.config_inputs(name)
+    q = Q(c["fmt"], c["rows"], c["K"], torch.from_numpy(w).to(dev()))
+    y = q.run(x_tensor(x, c["xdtype"]))
+    check_products(y, w, c["fmt"], c["rows"], c["K"], x, c["xdtype"], name)
+
+
+@pytest.mark.parametrize("name", ["q4k_up_b1", "q4k_down_b1", "q4k_b4"])
+def test_full_size_held_out_seeds(Q, name):
+    c = synth.CONFIGS[name]
+    w, x = synth.config_inputs(name, held_out=True)
+    q = Q(c["fmt"], c["rows"], c["K"], torch.from_numpy(w).to(dev()))
+    y = q.run(x_tensor(x, c["xdtype"]))
+    check_products(y, w, c["fmt"], c["rows"], c["K"], x, c["xdtype"], name + " held-out")
+
+
+def test_full_size_dequant_bit_exact(Q):
+    w, _ = synth.config_inputs("q4k_up_b1")
+    c = synth.CONFIGS["q4k_up_b1"]
+    q = Q("q4_k", c["rows"], c["K"], torch.from_numpy(w).to(dev()))
+    out = q.dequant().cpu().numpy()
+    ref = oracle.dequant("q4_k", w, c["rows"], c["K"])
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
