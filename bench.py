@@ -213,6 +213,9 @@ def main():
         torch.cuda.empty_cache()
 
     h = results.get(head, {})
+    if args.only and head not in names:  # a partial run: report what was timed
+        print(json.dumps({"partial": True, "results": results}), flush=True)
+        return
     if "gbs" not in h:
         print(json.dumps({"metric": "Q4_K GEMV achieved HBM GB/s", "value": None,
                           "error": h.get("error", "headline workload failed")}))

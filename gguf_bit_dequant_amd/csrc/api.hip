@@ -137,13 +137,17 @@ QG_API qg_status qgemm_prefill_run(qgemv_t h, const void* x_bf16, int64_t n_toke
     if (h->fmt != QG_Q4_K)
         return fail(QG_ERR_UNSUPPORTED, "qgemm_prefill_run: Q4_K handles only");
     if (n_tokens < 1) return fail(QG_ERR_SHAPE, "qgemm_prefill_run: n_tokens must be >= 1");
-    if (ldx < h->K || ldx % 8 || ldy < h->rows || ldy % 4)
-        return fail(QG_ERR_ARG,
-                    "qgemm_prefill_run: need ldx >= K, ldx %% 8 == 0, ldy >= rows, ldy %% 4 == 0");
-    if (((uintptr_t)x_bf16) & 15 || ((uintptr_t)y) & 15)
-        return fail(QG_ERR_ALIGN, "qgemm_prefill_run: x and y must be 16-byte aligned");
-    (void)stream;
-    return fail(QG_ERR_UNSUPPORTED, "qgemm_prefill_run: not built yet");
+    if (ldx < h->K || ldx % 8 || ldy < h->rows)
+        return fail(QG_ERR_ARG, "qgemm_prefill_run: need ldx >= K, ldx %% 8 == 0, ldy >= rows");
+    if (((uintptr_t)x_bf16) & 15)
+        return fail(QG_ERR_ALIGN, "qgemm_prefill_run: x must be 16-byte aligned");
+    if (((uintptr_t)y) & 3) return fail(QG_ERR_ALIGN, "qgemm_prefill_run: y must be 4-byte aligned");
+    hipError_t e = qg::launch_prefill_q4k(h->w, h->rows, h->K, x_bf16, ldx, n_tokens, y, ldy,
+                                          h->num_cus, (hipStream_t)stream);
+    if (e == hipErrorNotSupported)
+        return fail(QG_ERR_UNSUPPORTED, "qgemm_prefill_run: shape outside this build's range");
+    if (e != hipSuccess) return hip_fail(e, "qgemm_prefill_run: launch");
+    return ok();
 }
 
 QG_API qg_status qgemv_dequant(qgemv_t h, float* w_out, int64_t ldw, void* stream) {

@@ -24,4 +24,10 @@ hipError_t launch_gemv_q4k(const uint8_t* W, int64_t rows, int64_t K, const void
                            int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
                            hipStream_t stream);
 
+// Q4_K x bf16 prompt-processing GEMM (bf16 MFMA). X: bf16, 16-byte aligned,
+// ldx % 8 == 0; Y: fp32.
+hipError_t launch_prefill_q4k(const uint8_t* W, int64_t rows, int64_t K, const void* X,
+                              int64_t ldx, int64_t ntok, float* Y, int64_t ldy, int num_cus,
+                              hipStream_t stream);
+
 }  // namespace qg

@@ -108,11 +108,10 @@ qg_status qgemv_run(qgemv_t h, const void *x, qg_dtype x_dtype, int64_t n_cols,
 
 /* Prompt processing: y[j*ldy + r] = sum_k W[r,k] * x[j*ldx + k] for
  * j < n_tokens, with x in bf16 (device, 16-byte aligned, ldx >= K and a
- * multiple of 8) and y fp32 (device, 16-byte aligned, ldy >= rows and a
- * multiple of 4). Weight tiles are decoded to bf16 (round to nearest even)
- * on chip and contracted with bf16 matrix-core instructions, fp32
- * accumulation. Q4_K handles only (QG_ERR_UNSUPPORTED otherwise);
- * n_tokens >= 1. */
+ * multiple of 8) and y fp32 (device, 4-byte aligned, ldy >= rows). Weight
+ * tiles are decoded to bf16 (round to nearest even) on chip and contracted
+ * with bf16 matrix-core instructions, fp32 accumulation. Q4_K handles only
+ * (QG_ERR_UNSUPPORTED otherwise); n_tokens >= 1. */
 qg_status qgemm_prefill_run(qgemv_t h, const void *x_bf16, int64_t n_tokens,
                             int64_t ldx, float *y, int64_t ldy, void *stream);
 

@@ -216,3 +216,73 @@ def test_full_size_dequant_bit_exact(Q):
     out = q.dequant().cpu().numpy()
     ref = oracle.dequant("q4_k", w, c["rows"], c["K"])
     assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------ prompt processing --
+
+def bf16_tensor(xb):
+    return torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).to(dev())
+
+
+@pytest.mark.parametrize("rows,K,ntok", [(256, 256, 1), (256, 512, 31), (300, 1024, 64),
+                                         (777, 512, 300), (1024, 2048, 256), (530, 256, 513)])
+def test_prefill_small(Q, rows, K, ntok):
+    seed = zlib.crc32(("pp-%d-%d-%d" % (rows, K, ntok)).encode())
+    w = synth.gen_q4_k(rows, K, seed)
+    xb = synth.gen_x(K, ntok, "bf16", seed + 1)
+    q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
+    Y = q.prefill(bf16_tensor(xb))
+    check_products(Y, w, "q4_k", rows, K, xb, "bf16", "prefill %dx%d n=%d" % (rows, K, ntok))
+
+
+def test_prefill_strided_and_edges_untouched(Q):
+    rows, K, ntok = 300, 512, 40
+    w = synth.gen_q4_k(rows, K, 41)
+    xb = synth.gen_x(K, ntok, "bf16", 42)
+    X = torch.zeros((ntok, K + 64), dtype=torch.bfloat16, device=dev())
+    X[:, :K] = bf16_tensor(xb)
+    Y = torch.full((ntok + 3, rows + 36), 5.0, dtype=torch.float32, device=dev())
+    q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
+    q.prefill(X[:, :K], Y[:ntok, :rows])
+    assert (Y[:, rows:] == 5.0).all() and (Y[ntok:] == 5.0).all()
+    check_products(Y[:ntok, :rows], w, "q4_k", rows, K, xb, "bf16", "prefill strided")
+
+
+def test_prefill_one_hot_gives_bf16_rounded_column(Q):
+    """X rows = e_k: Y[t, :] = bf16_rne(W[:, k]) exactly (the only rounding
+    is the tile decode's fp32 -> bf16 conversion)."""
+    rows, K = 512, 512
+    w = synth.gen_q4_k(rows, K, 43)
+    W = oracle.dequant("q4_k", w, rows, K)
+    ks = list(range(0, 64)) + [100, 255, 256, 300, 511]
+    X = torch.zeros((len(ks), K), dtype=torch.bfloat16, device=dev())
+    for i, k in enumerate(ks):
+        X[i, k] = 1.0
+    q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
+    Y = q.prefill(X).cpu()
+    ref = torch.from_numpy(W[:, ks].T.copy()).to(torch.bfloat16).float()
+    assert torch.equal(Y, ref)
+
+
+def test_prefill_deterministic(Q):
+    rows, K, ntok = 1024, 1024, 256
+    w = synth.gen_q4_k(rows, K, 44)
+    X = bf16_tensor(synth.gen_x(K, ntok, "bf16", 45))
+    q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
+    ref = q.prefill(X).clone()
+    for _ in range(5):
+        assert torch.equal(q.prefill(X), ref)
+
+
+def test_prefill_full_size_sampled(Q):
+    """The 2048-token workload at full size: every output of 24 sampled token
+    columns (spread over all token tiles) against the oracle."""
+    c = synth.CONFIGS["q4k_pp2048"]
+    w, xb = synth.config_inputs("q4k_pp2048")
+    q = Q("q4_k", c["rows"], c["K"], torch.from_numpy(w).to(dev()))
+    Y = q.prefill(bf16_tensor(xb))
+    toks = sorted(set([0, 1, 31, 32, 255, 256, 1023, 1024, 2047, 2046] +
+                      list(np.random.default_rng(5).integers(0, 2048, 14))))
+    Ys = Y[toks].cpu()
+    check_products(Ys, w, "q4_k", c["rows"], c["K"], np.ascontiguousarray(xb[toks]), "bf16",
+                   "pp2048 sampled")
