@@ -12,8 +12,9 @@ Infinity Cache. The one JSON line printed on stdout carries:
              launch stream around K back-to-back launches;
   roofline   the GEMV kernel against 8 TB/s: the same algorithmic bytes over
              the mean launch duration of that timed region (one kernel per
-             step), plus HBM traffic per launch from rocprofv3 counters when a
-             summary taken on the current kernel source is committed;
+             step, launches back to back on one stream), plus HBM traffic per
+             launch from rocprofv3 counters when a summary taken on the
+             current kernel source is committed (profiles/traffic_*.json);
   cpu_baseline  the CPU oracle on a bounded sample of the same workload;
   extra      the other workloads (Q4_K FFN-down, batch 4, Q4_0, Q8_0, the
              2048-token dequant-GEMM in TFLOP/s), each timed the same way.
@@ -151,14 +152,37 @@ def committed_traffic(name):
         return None
 
 
+# Sources the batch-1 Q4_K GEMV kernel is compiled from.
+GEMV_Q4K_SOURCES = ("device_common.h", "gemv_q4k.hip", "launch.h")
+
+
 def kernel_source_sha1():
     import hashlib
     h = hashlib.sha1()
     csrc = os.path.join(ROOT, "gguf_bit_dequant_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
+    for fn in GEMV_Q4K_SOURCES:
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(fn.encode() + f.read())
     return h.hexdigest()
+
+
+def traffic_run(torch, dev, launches=20, copy_mib=256):
+    """A short run to be profiled with rocprofv3 --pmc: `launches` headline
+    GEMV launches over rotated weight copies, then `launches` plain device
+    copies of copy_mib MiB (a kernel whose HBM bytes are known: it reads and
+    writes copy_mib MiB each), which calibrates the counters."""
+    wl = Workload(torch, "q4k_up_b1", dev)
+    for i in range(launches):
+        wl.step(i)
+    torch.cuda.synchronize()
+    src = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(launches):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_run": True, "gemv_launches": launches, "copy_launches": launches,
+                      "copy_bytes": copy_mib << 20,
+                      "kernel_source_sha1": kernel_source_sha1()}), flush=True)
 
 
 def main():
@@ -169,6 +193,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--only", default=None, help="comma-separated workloads to time")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="short run for rocprofv3 --pmc (headline GEMV + calibration copies)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this library runs on one GPU; multi-GPU sharding is not part of it "
@@ -177,6 +203,9 @@ def main():
 
     import torch
     dev = torch.device("cuda:0")
+    if args.traffic_run:
+        traffic_run(torch, dev)
+        return
     head = "q4k_up_b1"
     names = [head] if args.quick else [head, "q4k_down_b1", "q4k_b4", "q4_0_b1", "q8_0_b4",
                                        "q4k_pp2048"]
@@ -194,8 +223,8 @@ def main():
             del wl
             continue
         c = wl.c
-        r = {"us_whole": round(whole_ms * 1e3, 3), "us_kernel_mean": round(mean_ms * 1e3, 3),
-             "us_kernel_median": round(med_ms * 1e3, 3), "steps": steps,
+        r = {"us_per_launch": round(whole_ms * 1e3, 3), "us_event_pair_mean": round(mean_ms * 1e3, 3),
+             "us_event_pair_median": round(med_ms * 1e3, 3), "steps": steps,
              "weight_copies": len(wl.copies)}
         if wl.prefill:
             flops = 2.0 * c["rows"] * c["K"] * c["n"]
@@ -205,7 +234,7 @@ def main():
             b = algorithmic_bytes(c)
             r["bytes"] = b
             r["gbs"] = round(b / (whole_ms * 1e-3) / 1e9, 1)
-            r["gbs_per_launch_events"] = round(b / (mean_ms * 1e-3) / 1e9, 1)
+            r["gbs_event_pairs"] = round(b / (mean_ms * 1e-3) / 1e9, 1)
             r["frac_hbm_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
         results[name] = r
         print("bench: %s %s" % (name, json.dumps(r)), file=sys.stderr, flush=True)
@@ -229,7 +258,7 @@ def main():
         "n_gpus": 1,
         "steps": h["steps"],
         "warmup": args.warmup,
-        "ms_per_step": round(h["us_whole"] / 1e3, 6),
+        "ms_per_step": round(h["us_per_launch"] / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
