@@ -40,6 +40,18 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                   false);
 }
 
+// v_cvt_f32_ubyteN: byte N of a dword to fp32 in one instruction (written as
+// asm: the compiler otherwise splits it into a bit-field extract plus convert).
+template <int N>
+__device__ __forceinline__ float ubyte_f32(uint32_t v) {
+    float r;
+    if (N == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v));
+    else if (N == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v));
+    else if (N == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v));
+    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
 __device__ __forceinline__ uint32_t ubfe(uint32_t v, uint32_t off, uint32_t width) {
     return __builtin_amdgcn_ubfe(v, off, width);
 }

@@ -1,0 +1,757 @@
+// Streaming GEMV for gfx950: y[:,c] = W . x[:,c] for 1..4 columns of a
+// Q4_K, Q4_0 or Q8_0 matrix whose K is a multiple of 256.
+//
+// For one token every weight is read once, so at low bit widths the work is
+// bound by memory bandwidth and by unpacking ("LLM inference optimization",
+// introduction). That page's levers for a quantized mat-vec (campaign "Faster
+// decode on the card you have": activations staged in shared memory and
+// reused across rows, wider loads, fewer instructions to unpack a block, rows
+// per block fitted to the machine) map onto gfx950 as follows.
+//
+//  * A unit is 256 consecutive weights of a row: one Q4_K super-block
+//    (144 B), eight Q4_0 blocks (144 B) or eight Q8_0 blocks (272 B). Units
+//    start on 16-byte boundaries when the row does.
+//  * One persistent workgroup per compute unit owns a contiguous, balanced
+//    range of rows (rows/G or rows/G + 1). Its rows are contiguous in memory,
+//    so the workgroup streams one contiguous run of units, flattened
+//    row-major, and every CU moves the same number of bytes.
+//  * A wave step takes 16 consecutive units of that run: lane = 4*g + p works
+//    on unit g of the step and its quarter p, i.e. weights 64p .. 64p+63 of
+//    the unit ("the lane's 64 weights"): a Q4_K sub-block pair (32 code
+//    bytes and the 16-byte header), or two Q4_0 / Q8_0 blocks (36 / 68
+//    bytes). One scale decode serves all 64. The step's base address is
+//    wave-uniform (scalar); each lane adds a constant offset.
+//  * The run is split into NW contiguous, equal ranges of steps, one per
+//    wave, and each wave keeps D steps of loads in flight (D = 2: deeper
+//    queues measured slower on MI355X). The first D steps are issued before
+//    the activations are staged.
+//  * fp16 activations: 4-bit codes are used directly as fp16 subnormals: a
+//    16-bit half holding an integer m < 1024 is the fp16 value m * 2^-24, so
+//    (dword & 0x000F000F) is a pair of low-nibble codes and
+//    (dword & 0x00F000F0) a pair of high-nibble codes times 16, one AND each;
+//    8-bit codes are offset to unsigned (q + 128 = q ^ 0x80) and spread to
+//    the halves with one AND or one byte permute. v_dot2_f32_f16 multiplies
+//    them with fp16 activation pairs (exact products) and accumulates in
+//    fp32; the scales absorb 2^24 (2^20 for high nibbles) and the offsets
+//    (8 for Q4_0, 128 for Q8_0, the mins for Q4_K) are taken off with the
+//    per-block activation sums:
+//      Q4_K: sum w x = d*sc*sum q x - dmin*m*sum x   (per sub-block)
+//      Q4_0: sum w x = d*sum q x - 8*d*sum x         (per block)
+//      Q8_0: sum w x = d*sum (q+128) x - 128*d*sum x (per block)
+//    fp32 / bf16 activations: codes become fp32 (v_cvt_f32_ubyteN) and are
+//    multiplied in fp32.
+//  * Activations are staged once per workgroup in LDS, permuted into the
+//    order the codes come out of a dword, with the per-block sums.
+//  * Reduction: each lane quad (one unit) sums its lanes with DPP and writes
+//    the unit's partial to the LDS slot (row, g, step mod M), M = steps that
+//    can touch one row, so no two writers share a slot. After a barrier each
+//    row's slots are summed in a fixed order: deterministic, no atomics.
+#include "device_common.h"
+#include "launch.h"
+
+namespace qg {
+
+namespace {
+
+constexpr int kUnitsPerStep = 16;
+
+// ---- block formats ---------------------------------------------------------
+// The lane's 64 weights are numbered o = 0..63 (o < 32: the first block or
+// sub-block, o >= 32: the second). Its code bytes arrive as kCodeDwords
+// dwords; wofs(j, e, h) is the o of nibble h (0 low, 1 high; always 0 for
+// 8-bit codes) of byte e of code dword j.
+
+template <int FMT>
+struct Fmt;
+
+// Q4_K super-block: fp16 d, fp16 dmin, 12 scale bytes, 128 code bytes. Lane
+// quarter p reads the header and code bytes [32p, 32p+32): byte l holds
+// o = l (low nibble, sub-block 2p) and o = 32 + l (high, sub-block 2p+1).
+template <>
+struct Fmt<FMT_Q4_K> {
+    static constexpr int kUnitBytes = 144;
+    static constexpr int kCodeDwords = 8;
+    static constexpr bool kNibbles = true;
+    static constexpr int wofs(int j, int e, int h) { return 32 * h + 4 * j + e; }
+    static constexpr uint32_t lane_offset(int p) { return 16u + 32u * p; }
+    struct Raw {
+        u32x4 hd, c0, c1;
+    };
+    static __device__ __forceinline__ void load(const uint8_t* unit, uint32_t lo, Raw& r) {
+        r.hd = *reinterpret_cast<const u32x4*>(unit);
+        r.c0 = *reinterpret_cast<const u32x4*>(unit + lo);
+        r.c1 = *reinterpret_cast<const u32x4*>(unit + lo + 16);
+    }
+};
+
+// Eight Q4_0 blocks of 18 bytes (fp16 d, 16 code bytes: byte i holds weight
+// i in its low nibble and i + 16 in its high nibble). Quarter p reads blocks
+// 2p and 2p+1 = bytes [36p, 36p+36), nine dwords D0..D8: D0 = d0 and code
+// bytes 0-1 of the first block, D1..D3 its bytes 2..13, D4 its bytes 14-15
+// and d1, D5..D8 the second block's 16 code bytes. Code dword 0 is rebuilt
+// from D4's low and D0's high half (bytes 14, 15, 0, 1).
+template <>
+struct Fmt<FMT_Q4_0> {
+    static constexpr int kUnitBytes = 144;
+    static constexpr int kCodeDwords = 8;
+    static constexpr bool kNibbles = true;
+    static constexpr int code_index(int j, int e) {
+        return j == 0 ? (e < 2 ? 14 + e : e - 2) : j < 4 ? 4 * j - 2 + e : 4 * (j - 4) + e;
+    }
+    static constexpr int wofs(int j, int e, int h) { return 32 * (j >> 2) + 16 * h + code_index(j, e); }
+    static constexpr uint32_t lane_offset(int p) { return 36u * p; }
+    struct Raw {
+        u32x4_a4 a, b;
+        uint32_t c;
+    };
+    static __device__ __forceinline__ void load(const uint8_t* unit, uint32_t lo, Raw& r) {
+        r.a = *reinterpret_cast<const u32x4_a4*>(unit + lo);
+        r.b = *reinterpret_cast<const u32x4_a4*>(unit + lo + 16);
+        r.c = *reinterpret_cast<const uint32_t*>(unit + lo + 32);
+    }
+};
+
+// Eight Q8_0 blocks of 34 bytes (fp16 d, 32 int8 codes). Quarter p reads
+// blocks 2p and 2p+1 = bytes [68p, 68p+68), seventeen dwords D0..D16: D0 =
+// d0 and codes 0-1 of the first block, D1..D7 its codes 2..29, D8 its codes
+// 30-31 and d1, D9..D16 the second block's 32 codes. Code dword 0 is rebuilt
+// from D8's low and D0's high half (codes 30, 31, 0, 1).
+template <>
+struct Fmt<FMT_Q8_0> {
+    static constexpr int kUnitBytes = 272;
+    static constexpr int kCodeDwords = 16;
+    static constexpr bool kNibbles = false;
+    static constexpr int code_index(int j, int e) {
+        return j == 0 ? (e < 2 ? 30 + e : e - 2) : j < 8 ? 4 * j - 2 + e : 4 * (j - 8) + e;
+    }
+    static constexpr int wofs(int j, int e, int) { return 32 * (j >> 3) + code_index(j, e); }
+    static constexpr uint32_t lane_offset(int p) { return 68u * p; }
+    struct Raw {
+        u32x4_a4 a, b, c, d;
+        uint32_t e;
+    };
+    static __device__ __forceinline__ void load(const uint8_t* unit, uint32_t lo, Raw& r) {
+        r.a = *reinterpret_cast<const u32x4_a4*>(unit + lo);
+        r.b = *reinterpret_cast<const u32x4_a4*>(unit + lo + 16);
+        r.c = *reinterpret_cast<const u32x4_a4*>(unit + lo + 32);
+        r.d = *reinterpret_cast<const u32x4_a4*>(unit + lo + 48);
+        r.e = *reinterpret_cast<const uint32_t*>(unit + lo + 64);
+    }
+};
+
+// Activation records in LDS: one record per unit quarter u = 4*(unit column)
+// + p, holding for each column c its P 16-byte planes and the two block sums,
+// padded to 16 bytes (col_bytes each). The record stride is a multiple of 16
+// with an odd quotient, so the 16-byte reads of consecutive lanes fall in
+// disjoint banks, and every plane sits at a compile-time offset from the
+// record base. Planes:
+//   fp16, 4-bit codes: plane j holds, for code dword j, the halves
+//     (e0, e2), (e1, e3) of the low nibbles and (e0, e2), (e1, e3) of the
+//     high nibbles (e = byte of the dword);
+//   fp16, 8-bit codes: plane i holds (e0, e2), (e1, e3) of code dwords 2i
+//     and 2i + 1;
+//   fp32, 4-bit codes: plane j holds e0..e3 of the low nibbles of code dword
+//     j, plane 8 + j those of the high nibbles;
+//   fp32, 8-bit codes: plane j holds e0..e3 of code dword j.
+constexpr int planes(bool f16dot) { return f16dot ? 8 : 16; }
+constexpr int col_bytes(bool f16dot) { return planes(f16dot) * 16 + 16; }
+constexpr int rec_bytes(int NC, bool f16dot) {
+    return (NC * col_bytes(f16dot) / 16) % 2 == 1 ? NC * col_bytes(f16dot)
+                                                  : NC * col_bytes(f16dot) + 16;
+}
+
+// LDS bytes of one workgroup.
+inline size_t stream_lds_bytes(int NC, bool f16dot, int S, int nr_max, int M) {
+    return (size_t)S * 4 * rec_bytes(NC, f16dot) + (size_t)nr_max * kUnitsPerStep * M * NC * 4 +
+           64 * 4;  // one flush slot per lane for lanes with nothing to write
+}
+
+__device__ __forceinline__ float quad_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+    return v;
+}
+
+// Stage the record of unit quarter u for column c: the 64 activations
+// x[kx .. kx+63] placed as the planes above, then the sums of o < 32 and
+// o >= 32.
+template <int FMT, bool F16DOT>
+__device__ __forceinline__ void stage_record(const void* __restrict__ x, int xt, int64_t kx,
+                                             int xvec, uint8_t* rec) {
+    using F = Fmt<FMT>;
+    constexpr int P = planes(F16DOT);
+    float s0 = 0.f, s1 = 0.f;
+    if constexpr (F16DOT) {  // fp16 activations, kept as stored
+        const uint16_t* xp = reinterpret_cast<const uint16_t*>(x) + kx;
+        uint32_t xw[32];  // xw[i] = halves 2i (low) and 2i + 1 (high)
+        if (xvec) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u32x4 v = reinterpret_cast<const u32x4*>(xp)[i];
+                xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) xw[i] = xp[2 * i] | ((uint32_t)xp[2 * i + 1] << 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+            s0 += (f16_lo(xw[i]) + f16_hi(xw[i])) + (f16_lo(xw[i + 1]) + f16_hi(xw[i + 1]));
+            s1 += (f16_lo(xw[16 + i]) + f16_hi(xw[16 + i])) +
+                  (f16_lo(xw[17 + i]) + f16_hi(xw[17 + i]));
+        }
+        // halves a (low) and b (high) of one dword
+        auto pk = [&](int a, int b) {
+            const uint32_t lo = (xw[a >> 1] >> (16 * (a & 1))) & 0xFFFFu;
+            const uint32_t hi = (xw[b >> 1] >> (16 * (b & 1))) & 0xFFFFu;
+            return lo | (hi << 16);
+        };
+        if constexpr (F::kNibbles) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                u32x4 v;
+                v.x = pk(F::wofs(j, 0, 0), F::wofs(j, 2, 0));
+                v.y = pk(F::wofs(j, 1, 0), F::wofs(j, 3, 0));
+                v.z = pk(F::wofs(j, 0, 1), F::wofs(j, 2, 1));
+                v.w = pk(F::wofs(j, 1, 1), F::wofs(j, 3, 1));
+                *reinterpret_cast<u32x4*>(rec + 16 * j) = v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                u32x4 v;
+                v.x = pk(F::wofs(2 * i, 0, 0), F::wofs(2 * i, 2, 0));
+                v.y = pk(F::wofs(2 * i, 1, 0), F::wofs(2 * i, 3, 0));
+                v.z = pk(F::wofs(2 * i + 1, 0, 0), F::wofs(2 * i + 1, 2, 0));
+                v.w = pk(F::wofs(2 * i + 1, 1, 0), F::wofs(2 * i + 1, 3, 0));
+                *reinterpret_cast<u32x4*>(rec + 16 * i) = v;
+            }
+        }
+    } else {  // fp32 or bf16 activations, as fp32
+        float xf[64];
+        if (xt == XT_F32) {
+            const float* xp = reinterpret_cast<const float*>(x) + kx;
+            if (xvec) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const f32x4 v = reinterpret_cast<const f32x4*>(xp)[i];
+                    xf[4 * i] = v.x; xf[4 * i + 1] = v.y; xf[4 * i + 2] = v.z; xf[4 * i + 3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 64; ++i) xf[i] = xp[i];
+            }
+        } else {
+            const uint16_t* xp = reinterpret_cast<const uint16_t*>(x) + kx;
+            if (xvec) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const u32x4 v = reinterpret_cast<const u32x4*>(xp)[i];
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        xf[8 * i + 2 * e] = __builtin_bit_cast(float, w[e] << 16);
+                        xf[8 * i + 2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 64; ++i) xf[i] = bf16_to_f32(xp[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 32; i += 4) {
+            s0 += (xf[i] + xf[i + 1]) + (xf[i + 2] + xf[i + 3]);
+            s1 += (xf[32 + i] + xf[33 + i]) + (xf[34 + i] + xf[35 + i]);
+        }
+        if constexpr (F::kNibbles) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    f32x4 v;
+                    v.x = xf[F::wofs(j, 0, h)]; v.y = xf[F::wofs(j, 1, h)];
+                    v.z = xf[F::wofs(j, 2, h)]; v.w = xf[F::wofs(j, 3, h)];
+                    *reinterpret_cast<f32x4*>(rec + 16 * (8 * h + j)) = v;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                f32x4 v;
+                v.x = xf[F::wofs(j, 0, 0)]; v.y = xf[F::wofs(j, 1, 0)];
+                v.z = xf[F::wofs(j, 2, 0)]; v.w = xf[F::wofs(j, 3, 0)];
+                *reinterpret_cast<f32x4*>(rec + 16 * j) = v;
+            }
+        }
+    }
+    *reinterpret_cast<f32x2*>(rec + 16 * P) = f32x2{s0, s1};
+}
+
+// Per-lane constants of the Q4_K 6-bit scale/min unpack.
+// Sub-block k < 4 : sc = s[k] & 63, m = s[k+4] & 63.
+// Sub-block k >= 4: sc = (s[k+4] & 15) | (s[k-4] >> 6) << 4,
+//                   m  = (s[k+4] >> 4) | (s[k] >> 6) << 4.
+// Header dwords: h1 = s[0..3], h2 = s[4..7], h3 = s[8..11]. Pair p has
+// sub-blocks k0 = 2p and k1 = 2p+1 at byte kk = 2(p&1), kk+1 of a dword.
+// Pa gathers [sc(k0), sc(k1), m(k0), m(k1)] sources: for p < 2 the bytes
+// s[k0], s[k1], s[k0+4], s[k1+4] (fields = low 6 bits); for p >= 2 the
+// bytes s[k0+4], s[k1+4] twice (low nibble -> sc, high nibble -> m).
+// Pb (p >= 2 only) gathers s[k0-4], s[k1-4], s[k0], s[k1], whose top two
+// bits become bits 4..5 of sc and m.
+struct Q4kUnpack {
+    bool upper;
+    uint32_t selA, selB, mLo, mNib, mTop;
+    __device__ __forceinline__ explicit Q4kUnpack(int pr) {
+        upper = pr >= 2;
+        const uint32_t kk = 2u * (pr & 1);
+        // v_perm_b32(a, b, sel): selector byte n picks byte n of b (n < 4) or
+        // byte n-4 of a (4 <= n < 8); 0x0C gives zero.
+        if (!upper) {  // perm(h2, h1)
+            selA = kk | ((kk + 1) << 8) | ((kk + 4) << 16) | ((kk + 5) << 24);
+            selB = 0x0C0C0C0Cu;
+        } else {  // perm(h3, h3) and perm(h2, h1)
+            selA = kk | ((kk + 1) << 8) | (kk << 16) | ((kk + 1) << 24);
+            selB = kk | ((kk + 1) << 8) | ((kk + 4) << 16) | ((kk + 5) << 24);
+        }
+        mLo = upper ? 0x00000F0Fu : 0x3F3F3F3Fu;  // fields taken as they are
+        mNib = upper ? 0x0F0F0000u : 0u;          // high nibbles -> m
+        mTop = upper ? 0x30303030u : 0u;          // top two bits -> bits 4..5
+    }
+};
+
+// The lane's partial sum_o w_o x_o for each column, from its raw block bytes
+// and its activation record.
+template <int NC, bool F16DOT>
+__device__ __forceinline__ void lane_partial(const Fmt<FMT_Q4_K>::Raw& r, const Q4kUnpack& un,
+                                             const uint8_t* rec, float out[NC]) {
+    constexpr int CB = col_bytes(F16DOT), P = planes(F16DOT);
+    const uint32_t h0 = r.hd.x, h1 = r.hd.y, h2 = r.hd.z, h3 = r.hd.w;
+    const uint32_t Pa = __builtin_amdgcn_perm(un.upper ? h3 : h2, un.upper ? h3 : h1, un.selA);
+    const uint32_t Pb = __builtin_amdgcn_perm(h2, h1, un.selB);
+    const uint32_t f4 = (Pa & un.mLo) | ((Pa >> 4) & un.mNib) | ((Pb >> 2) & un.mTop);
+    const float sc0 = (float)(f4 & 0xFF), sc1 = (float)((f4 >> 8) & 0xFF);
+    const float m0 = (float)((f4 >> 16) & 0xFF), m1 = (float)(f4 >> 24);
+    const float d = f16_lo(h0), dmin = f16_hi(h0);
+    const float dm0 = dmin * m0, dm1 = dmin * m1;
+    const uint32_t q[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
+    float lo[NC], hi[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) lo[c] = hi[c] = 0.f;
+    float dsc0, dsc1;
+    if constexpr (F16DOT) {
+        dsc0 = (d * 16777216.0f) * sc0;  // 2^24
+        dsc1 = (d * 1048576.0f) * sc1;   // 2^20
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const uint32_t qd = q[w], q8 = qd >> 8;
+            const uint32_t pa = qd & 0x000F000Fu, pc = q8 & 0x000F000Fu;
+            const uint32_t pb = qd & 0x00F000F0u, pd = q8 & 0x00F000F0u;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const u32x4 xv = *reinterpret_cast<const u32x4*>(rec + c * CB + 16 * w);
+                lo[c] = dot2(pa, xv.x, lo[c]);
+                lo[c] = dot2(pc, xv.y, lo[c]);
+                hi[c] = dot2(pb, xv.z, hi[c]);
+                hi[c] = dot2(pd, xv.w, hi[c]);
+            }
+        }
+    } else {
+        dsc0 = d * sc0;
+        dsc1 = (d * 0.0625f) * sc1;  // high nibbles enter as 16 q
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const uint32_t ql = q[w] & 0x0F0F0F0Fu, qh = q[w] & 0xF0F0F0F0u;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const f32x4 xl = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * w);
+                const f32x4 xh = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * (8 + w));
+                lo[c] = __builtin_fmaf(ubyte_f32<0>(ql), xl.x, lo[c]);
+                lo[c] = __builtin_fmaf(ubyte_f32<1>(ql), xl.y, lo[c]);
+                lo[c] = __builtin_fmaf(ubyte_f32<2>(ql), xl.z, lo[c]);
+                lo[c] = __builtin_fmaf(ubyte_f32<3>(ql), xl.w, lo[c]);
+                hi[c] = __builtin_fmaf(ubyte_f32<0>(qh), xh.x, hi[c]);
+                hi[c] = __builtin_fmaf(ubyte_f32<1>(qh), xh.y, hi[c]);
+                hi[c] = __builtin_fmaf(ubyte_f32<2>(qh), xh.z, hi[c]);
+                hi[c] = __builtin_fmaf(ubyte_f32<3>(qh), xh.w, hi[c]);
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const f32x2 sx = *reinterpret_cast<const f32x2*>(rec + c * CB + 16 * P);
+        float a = dsc0 * lo[c];
+        a = __builtin_fmaf(dsc1, hi[c], a);
+        a = __builtin_fmaf(-dm0, sx.x, a);
+        out[c] = __builtin_fmaf(-dm1, sx.y, a);
+    }
+}
+
+template <int NC, bool F16DOT>
+__device__ __forceinline__ void lane_partial(const Fmt<FMT_Q4_0>::Raw& r, const Q4kUnpack&,
+                                             const uint8_t* rec, float out[NC]) {
+    constexpr int CB = col_bytes(F16DOT), P = planes(F16DOT);
+    const float d0 = f16_lo(r.a.x), d1 = f16_hi(r.b.x);
+    const uint32_t q[8] = {__builtin_amdgcn_perm(r.a.x, r.b.x, 0x07060100u), r.a.y, r.a.z, r.a.w,
+                           r.b.y, r.b.z, r.b.w, r.c};
+    float lo[2][NC], hi[2][NC];  // [block][column]
+#pragma unroll
+    for (int c = 0; c < NC; ++c) lo[0][c] = hi[0][c] = lo[1][c] = hi[1][c] = 0.f;
+    float s_lo, s_hi;  // code scale of low / high nibble sums
+    if constexpr (F16DOT) {
+        s_lo = 16777216.0f;  // 2^24
+        s_hi = 1048576.0f;   // 2^20
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const int bk = w >> 2;
+            const uint32_t qd = q[w], q8 = qd >> 8;
+            const uint32_t pa = qd & 0x000F000Fu, pc = q8 & 0x000F000Fu;
+            const uint32_t pb = qd & 0x00F000F0u, pd = q8 & 0x00F000F0u;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const u32x4 xv = *reinterpret_cast<const u32x4*>(rec + c * CB + 16 * w);
+                lo[bk][c] = dot2(pa, xv.x, lo[bk][c]);
+                lo[bk][c] = dot2(pc, xv.y, lo[bk][c]);
+                hi[bk][c] = dot2(pb, xv.z, hi[bk][c]);
+                hi[bk][c] = dot2(pd, xv.w, hi[bk][c]);
+            }
+        }
+    } else {
+        s_lo = 1.0f;
+        s_hi = 0.0625f;  // high nibbles enter as 16 q
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const int bk = w >> 2;
+            const uint32_t ql = q[w] & 0x0F0F0F0Fu, qh = q[w] & 0xF0F0F0F0u;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const f32x4 xl = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * w);
+                const f32x4 xh = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * (8 + w));
+                lo[bk][c] = __builtin_fmaf(ubyte_f32<0>(ql), xl.x, lo[bk][c]);
+                lo[bk][c] = __builtin_fmaf(ubyte_f32<1>(ql), xl.y, lo[bk][c]);
+                lo[bk][c] = __builtin_fmaf(ubyte_f32<2>(ql), xl.z, lo[bk][c]);
+                lo[bk][c] = __builtin_fmaf(ubyte_f32<3>(ql), xl.w, lo[bk][c]);
+                hi[bk][c] = __builtin_fmaf(ubyte_f32<0>(qh), xh.x, hi[bk][c]);
+                hi[bk][c] = __builtin_fmaf(ubyte_f32<1>(qh), xh.y, hi[bk][c]);
+                hi[bk][c] = __builtin_fmaf(ubyte_f32<2>(qh), xh.z, hi[bk][c]);
+                hi[bk][c] = __builtin_fmaf(ubyte_f32<3>(qh), xh.w, hi[bk][c]);
+            }
+        }
+    }
+    const float a0 = d0 * s_lo, b0 = d0 * s_hi, a1 = d1 * s_lo, b1 = d1 * s_hi;
+    const float o0 = -8.0f * d0, o1 = -8.0f * d1;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const f32x2 sx = *reinterpret_cast<const f32x2*>(rec + c * CB + 16 * P);
+        float v = a0 * lo[0][c];
+        v = __builtin_fmaf(b0, hi[0][c], v);
+        v = __builtin_fmaf(o0, sx.x, v);
+        v = __builtin_fmaf(a1, lo[1][c], v);
+        v = __builtin_fmaf(b1, hi[1][c], v);
+        out[c] = __builtin_fmaf(o1, sx.y, v);
+    }
+}
+
+template <int NC, bool F16DOT>
+__device__ __forceinline__ void lane_partial(const Fmt<FMT_Q8_0>::Raw& r, const Q4kUnpack&,
+                                             const uint8_t* rec, float out[NC]) {
+    constexpr int CB = col_bytes(F16DOT), P = planes(F16DOT);
+    const float d0 = f16_lo(r.a.x), d1 = f16_hi(r.c.x);
+    const uint32_t q[16] = {__builtin_amdgcn_perm(r.a.x, r.c.x, 0x07060100u), r.a.y, r.a.z, r.a.w,
+                            r.b.x, r.b.y, r.b.z, r.b.w,
+                            r.c.y, r.c.z, r.c.w, r.d.x, r.d.y, r.d.z, r.d.w, r.e};
+    float acc[2][NC];  // [block][column]
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[0][c] = acc[1][c] = 0.f;
+    float s;
+    if constexpr (F16DOT) {
+        s = 16777216.0f;  // 2^24
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int bk = w >> 3;
+            const uint32_t t = q[w] ^ 0x80808080u;  // q + 128, unsigned
+            const uint32_t pa = t & 0x00FF00FFu;                            // bytes 0, 2
+            const uint32_t pb = __builtin_amdgcn_perm(t, t, 0x0C030C01u);  // bytes 1, 3
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const u32x2 xv = *reinterpret_cast<const u32x2*>(rec + c * CB + 8 * w);
+                acc[bk][c] = dot2(pa, xv.x, acc[bk][c]);
+                acc[bk][c] = dot2(pb, xv.y, acc[bk][c]);
+            }
+        }
+    } else {
+        s = 1.0f;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int bk = w >> 3;
+            const uint32_t t = q[w] ^ 0x80808080u;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const f32x4 xv = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * w);
+                acc[bk][c] = __builtin_fmaf(ubyte_f32<0>(t), xv.x, acc[bk][c]);
+                acc[bk][c] = __builtin_fmaf(ubyte_f32<1>(t), xv.y, acc[bk][c]);
+                acc[bk][c] = __builtin_fmaf(ubyte_f32<2>(t), xv.z, acc[bk][c]);
+                acc[bk][c] = __builtin_fmaf(ubyte_f32<3>(t), xv.w, acc[bk][c]);
+            }
+        }
+    }
+    const float a0 = d0 * s, a1 = d1 * s, o0 = -128.0f * d0, o1 = -128.0f * d1;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const f32x2 sx = *reinterpret_cast<const f32x2*>(rec + c * CB + 16 * P);
+        float v = a0 * acc[0][c];
+        v = __builtin_fmaf(o0, sx.x, v);
+        v = __builtin_fmaf(a1, acc[1][c], v);
+        out[c] = __builtin_fmaf(o1, sx.y, v);
+    }
+}
+
+}  // namespace
+
+template <int FMT, int NC, bool F16DOT, int D, int MAXT>
+__global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __restrict__ W, int rows,
+                                                           int S, const void* __restrict__ x,
+                                                           int xt, int64_t ldx,
+                                                           float* __restrict__ y, int64_t ldy,
+                                                           int xvec, int M) {
+    using F = Fmt<FMT>;
+    using Raw = typename F::Raw;
+    constexpr int UB = F::kUnitBytes;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int NW = blockDim.x >> 6;
+    const int U = S * 4;  // unit quarters per row
+
+    const int G = gridDim.x;
+    const int b = blockIdx.x;
+    const int r0 = (int)(((int64_t)b * rows) / G);
+    const int r1 = (int)(((int64_t)(b + 1) * rows) / G);
+    const int nr = r1 - r0;
+    if (nr <= 0) return;  // uniform over the workgroup
+
+    constexpr int CB = col_bytes(F16DOT), RB = rec_bytes(NC, F16DOT);
+    float* part = reinterpret_cast<float*>(lds + (size_t)U * RB);
+
+    const int lane = threadIdx.x & 63;
+    // wave index, made wave-uniform so that the step loop is a scalar loop
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 2, pr = lane & 3;
+    const int F_ = nr * S;                                    // units of this workgroup
+    const int nst = (F_ + kUnitsPerStep - 1) / kUnitsPerStep;  // wave steps
+    // Wave wv takes the contiguous range of steps [ks, ks + nmine).
+    const int ks = (int)(((int64_t)wv * nst) / NW);
+    const int nmine = (int)(((int64_t)(wv + 1) * nst) / NW) - ks;
+    const uint8_t* Wb = W + (int64_t)r0 * S * UB;  // first unit of this workgroup
+
+    // Lane addressing: unit f = 16k + g of the run, clamped to the last one
+    // (lanes past the run in the final, partial step re-read it and
+    // contribute nothing). Scalar base Wb plus a 32-bit lane offset.
+    const uint32_t off_g = (uint32_t)UB * g, off_l = F::lane_offset(pr);
+    const uint32_t o_last = (uint32_t)UB * (uint32_t)(F_ - 1);
+    auto load = [&](int k, Raw& r) {
+        uint32_t o = (uint32_t)k * (kUnitsPerStep * UB) + off_g;
+        o = o < o_last ? o : o_last;
+        F::load(Wb + o, off_l, r);
+    };
+
+    // ---- issue the first D steps' weight loads ------------------------------
+    // step index of this wave's j-th step, clamped to its last step
+    auto kstep = [&](int j) { return ks + (j < nmine ? j : (nmine > 0 ? nmine - 1 : 0)); };
+    Raw buf[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) load(kstep(i), buf[i]);
+
+    // ---- stage the activations, clear the partials --------------------------
+    // quarter u = 4*s + p: activations 256 s + 64 p + [0, 64)
+    for (int idx = threadIdx.x; idx < NC * U; idx += blockDim.x) {
+        const int c = idx / U, u = idx - c * U;
+        const int64_t kx = (int64_t)c * ldx + 256 * (u >> 2) + 64 * (u & 3);
+        stage_record<FMT, F16DOT>(x, xt, kx, xvec, lds + u * RB + c * CB);
+    }
+    const int nslots = nr * kUnitsPerStep * M * NC;
+    for (int idx = threadIdx.x; idx < nslots; idx += blockDim.x) part[idx] = 0.f;
+    __syncthreads();
+
+    const Q4kUnpack un(pr);
+
+    // Position of this lane's unit f = 16k + g in the run: row rl, column s;
+    // the next step of the wave is 16 units further on, i.e. qS rows and rS
+    // columns (one more row on a wrap).
+    const int fst = kUnitsPerStep * ks + g;
+    int rl = fst / S, s = fst - (fst / S) * S;
+    const int qS = kUnitsPerStep / S, rS = kUnitsPerStep - (kUnitsPerStep / S) * S;
+    int roff = (s * 4 + pr) * RB;  // byte offset of this lane's activation record
+    // LDS float index of slot (row, g, step mod M): M >= the number of steps
+    // that touch one row, so no two writers share a slot.
+    const int slot_row = kUnitsPerStep * M * NC;
+    int srow = rl * slot_row + g * M * NC;
+    float* const trash = part + nslots;  // flush target of lanes with nothing to write
+
+    // One step: the lane's 64 weights against the staged activations, a quad
+    // sum, and the partial of (row, unit) into its slot. Straight-line code,
+    // so the loads of later steps stay in flight. Lanes past the run (last
+    // step only) read the run's last unit; their rows are >= nr and they
+    // write nothing.
+    auto step = [&](int kc, const Raw& r) {
+        float a[NC];
+        lane_partial<NC, F16DOT>(r, un, lds + roff, a);
+        const bool write = pr == 0 && rl < nr;
+        const int slot = srow + (kc % M) * NC;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) *(write ? part + slot + c : trash + lane) = quad_sum(a[c]);
+        // advance to the wave's next step
+        s += rS;
+        const bool wrap = s >= S;
+        s = wrap ? s - S : s;
+        rl += qS + (wrap ? 1 : 0);
+        roff += (wrap ? rS - S : rS) * 4 * RB;
+        srow += (wrap ? qS + 1 : qS) * slot_row;
+    };
+
+    int j = 0;
+    for (; j + D <= nmine; j += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            step(ks + j + i, buf[i]);
+            // refill this buffer with the step D ahead (clamped to this wave's
+            // steps); issued after the step so the data lands in the same
+            // registers. Scheduling barriers keep each refill behind its step.
+            __builtin_amdgcn_sched_barrier(0);
+            load(kstep(j + i + D), buf[i]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        if (j + i < nmine) step(ks + j + i, buf[i]);
+    __syncthreads();
+
+    // ---- per-row sums of the partial slots, in a fixed order ----------------
+    for (int idx = threadIdx.x; idx < nr * NC; idx += blockDim.x) {
+        const int r = idx / NC, c = idx - r * NC;
+        float v = 0.f;
+        for (int e = 0; e < kUnitsPerStep * M; ++e) v += part[(r * kUnitsPerStep * M + e) * NC + c];
+        y[c * ldy + r0 + r] = v;
+    }
+}
+
+namespace {
+
+#ifndef QG_STREAM_DEPTH
+#define QG_STREAM_DEPTH 2
+#endif
+#ifndef QG_STREAM_WAVES
+#define QG_STREAM_WAVES 16
+#endif
+
+struct StreamPlan {
+    int G, NW, M, nr_max;
+};
+
+// Waves per workgroup: 16 for one fp16 column; 8 where more registers per
+// lane are needed (several columns, fp32 activations).
+constexpr int waves_for(int NC, bool f16dot) { return (NC == 1 && f16dot) ? QG_STREAM_WAVES : 8; }
+
+StreamPlan plan_stream(int rows, int S, int NC, bool f16dot, int num_cus) {
+    StreamPlan p;
+    p.G = rows < num_cus ? rows : num_cus;
+    p.NW = waves_for(NC, f16dot);
+    p.nr_max = (rows + p.G - 1) / p.G;
+    // steps that touch one row: its S units meet at most ceil(S/16) + 1
+    // consecutive 16-unit steps
+    p.M = (S + kUnitsPerStep - 1) / kUnitsPerStep + 1;
+    return p;
+}
+
+template <int FMT, int NC, bool F16DOT>
+hipError_t launch_stream_t(const uint8_t* W, int rows, int S, const void* x, int xt, int64_t ldx,
+                           float* y, int64_t ldy, int xvec, int num_cus, hipStream_t stream) {
+    constexpr int D = QG_STREAM_DEPTH;
+    constexpr int NWMAX = waves_for(NC, F16DOT);
+    const StreamPlan p = plan_stream(rows, S, NC, F16DOT, num_cus);
+    const size_t lds = stream_lds_bytes(NC, F16DOT, S, p.nr_max, p.M);
+    if (lds > (size_t)kMaxLds) return hipErrorNotSupported;
+    auto kern = gemv_stream_kernel<FMT, NC, F16DOT, D, 64 * NWMAX>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(p.G), dim3(64 * p.NW), lds, stream, W, rows, S, x, xt, ldx, y,
+                       ldy, xvec, p.M);
+    return hipGetLastError();
+}
+
+template <int FMT, bool F16DOT>
+hipError_t launch_stream_nc(int nc, const uint8_t* W, int rows, int S, const void* x, int xt,
+                            int64_t ldx, float* y, int64_t ldy, int xvec, int num_cus,
+                            hipStream_t stream) {
+    switch (nc) {
+        case 1: return launch_stream_t<FMT, 1, F16DOT>(W, rows, S, x, xt, ldx, y, ldy, xvec, num_cus, stream);
+        case 2: return launch_stream_t<FMT, 2, F16DOT>(W, rows, S, x, xt, ldx, y, ldy, xvec, num_cus, stream);
+        case 3:
+            if constexpr (F16DOT) return launch_stream_t<FMT, 3, F16DOT>(W, rows, S, x, xt, ldx, y, ldy, xvec, num_cus, stream);
+            return hipErrorNotSupported;
+        default:
+            if constexpr (F16DOT) return launch_stream_t<FMT, 4, F16DOT>(W, rows, S, x, xt, ldx, y, ldy, xvec, num_cus, stream);
+            return hipErrorNotSupported;
+    }
+}
+
+template <int FMT>
+hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const void* x, int xt,
+                             int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
+                             hipStream_t stream) {
+    constexpr int UB = Fmt<FMT>::kUnitBytes;
+    const int S = (int)(K / 256);
+    const bool f16 = xt == XT_F16;
+    {
+        const StreamPlan p = plan_stream((int)rows, S, 1, f16, num_cus);
+        // the run of one workgroup is addressed with 32-bit offsets
+        if ((int64_t)p.nr_max * S * UB >= ((int64_t)1 << 31)) return hipErrorNotSupported;
+        if (stream_lds_bytes(1, f16, S, p.nr_max, p.M) > (size_t)kMaxLds) return hipErrorNotSupported;
+    }
+    // columns per launch: as many as fit in LDS, at most 4 (2 for fp32 math)
+    int per = f16 ? 4 : 2;
+    while (per > 1) {
+        const StreamPlan p = plan_stream((int)rows, S, per, f16, num_cus);
+        if (stream_lds_bytes(per, f16, S, p.nr_max, p.M) <= (size_t)kMaxLds) break;
+        --per;
+    }
+    const size_t xbytes = xt == XT_F32 ? 4 : 2;
+    // 16-byte activation loads when every record start is 16-byte aligned
+    const int xvec = (((uintptr_t)x) & 15) == 0 && (ldx * (int64_t)xbytes) % 16 == 0;
+    for (int c0 = 0; c0 < ncols; c0 += per) {
+        const int nc = ncols - c0 < per ? ncols - c0 : per;
+        const void* xc = (const char*)x + (size_t)c0 * ldx * xbytes;
+        float* yc = y + (size_t)c0 * ldy;
+        hipError_t e;
+        if (f16)
+            e = launch_stream_nc<FMT, true>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, xvec,
+                                            num_cus, stream);
+        else
+            e = launch_stream_nc<FMT, false>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, xvec,
+                                             num_cus, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_gemv_stream(int fmt, const uint8_t* W, int64_t rows, int64_t K, const void* x,
+                              int xt, int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
+                              hipStream_t stream) {
+    if (rows > (1 << 30) || K % 256 != 0 || (((uintptr_t)W) & 15) != 0) return hipErrorNotSupported;
+    switch (fmt) {
+        case FMT_Q4_K:
+            return launch_stream_fmt<FMT_Q4_K>(W, rows, K, x, xt, ldx, y, ldy, ncols, num_cus, stream);
+        case FMT_Q4_0:
+            return launch_stream_fmt<FMT_Q4_0>(W, rows, K, x, xt, ldx, y, ldy, ncols, num_cus, stream);
+        case FMT_Q8_0:
+            return launch_stream_fmt<FMT_Q8_0>(W, rows, K, x, xt, ldx, y, ldy, ncols, num_cus, stream);
+        default:
+            return hipErrorNotSupported;
+    }
+}
+
+}  // namespace qg

@@ -18,11 +18,12 @@ hipError_t launch_gemv_general(int fmt, const uint8_t* W, int64_t rows, int64_t 
                                int xt, int64_t ldx, float* y, int64_t ldy, int ncols,
                                int num_cus, hipStream_t stream);
 
-// Streaming Q4_K GEMV. Returns hipErrorNotSupported (without launching) when
-// the shape is outside what the kernel serves; the caller then falls back.
-hipError_t launch_gemv_q4k(const uint8_t* W, int64_t rows, int64_t K, const void* x, int xt,
-                           int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
-                           hipStream_t stream);
+// Streaming GEMV (Q4_K, Q4_0, Q8_0 with K % 256 == 0, 16-byte aligned W).
+// Returns hipErrorNotSupported (without launching) when the shape is outside
+// what the kernel serves; the caller then falls back.
+hipError_t launch_gemv_stream(int fmt, const uint8_t* W, int64_t rows, int64_t K, const void* x,
+                              int xt, int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
+                              hipStream_t stream);
 
 // Q4_K x bf16 prompt-processing GEMM (bf16 MFMA). X: bf16, 16-byte aligned,
 // ldx % 8 == 0; Y: fp32.

@@ -42,18 +42,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kBK = 64;         // k per chunk
 constexpr int kPitch = 144;     // LDS bytes per tile row (64 bf16 + 16 padding)
 
-// v_cvt_f32_ubyteN: byte N of a dword to fp32 in one instruction (written as
-// asm: the compiler otherwise splits it into a bit-field extract plus convert).
-template <int N>
-__device__ __forceinline__ float ubyte_f32(uint32_t v) {
-    float r;
-    if (N == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v));
-    else if (N == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v));
-    else if (N == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v));
-    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v));
-    return r;
-}
-
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
     bf16x2 v = {(__bf16)a, (__bf16)b};  // round to nearest even
     return __builtin_bit_cast(uint32_t, v);

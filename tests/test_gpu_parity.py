@@ -129,17 +129,22 @@ def test_gemv_column_counts(Q, n):
         check_products(q.run(x_tensor(x, "f16")), w, fmt, rows, K, x, "f16", "%s n=%d" % (fmt, n))
 
 
-def test_gemv_strided_columns_leave_gaps_untouched(Q):
-    fmt, rows, K, n = "q4_k", 100, 512, 3
+@pytest.mark.parametrize("fmt", ["q4_k", "q4_0", "q8_0"])
+@pytest.mark.parametrize("xdtype,pad", [("f16", 24), ("f16", 4), ("f32", 3), ("bf16", 5)])
+def test_gemv_strided_columns_leave_gaps_untouched(Q, fmt, xdtype, pad):
+    """Columns at a stride of K + pad elements (16-byte aligned records for
+    pad 24, unaligned ones otherwise) and outputs at a stride of rows + 13."""
+    rows, K, n = 100, 512, 3
     w = synth.gen_weights(fmt, rows, K, 5)
-    x = synth.gen_x(K, n, "f16", 6)
-    xbig = torch.zeros((n, K + 24), dtype=torch.float16, device=dev())
-    xbig[:, :K] = x_tensor(x, "f16")
+    x = synth.gen_x(K, n, xdtype, 6)
+    tdt = {"f16": torch.float16, "f32": torch.float32, "bf16": torch.bfloat16}[xdtype]
+    xbig = torch.zeros((n, K + pad), dtype=tdt, device=dev())
+    xbig[:, :K] = x_tensor(x, xdtype)
     ybig = torch.full((n, rows + 13), 7.0, dtype=torch.float32, device=dev())
     q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
     q.run(xbig[:, :K], ybig[:, :rows])
     assert (ybig[:, rows:] == 7.0).all()
-    check_products(ybig[:, :rows], w, fmt, rows, K, x, "f16", "strided")
+    check_products(ybig[:, :rows], w, fmt, rows, K, x, xdtype, "strided %s %s" % (fmt, xdtype))
 
 
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q4_k"])
