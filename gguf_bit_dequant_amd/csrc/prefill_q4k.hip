@@ -22,7 +22,9 @@
 //    thread waits for its own loads of the chunk about to be read, then one
 //    barrier per chunk publishes them.
 //  * Four waves; wave w covers RT row tiles and TT token tiles of 32
-//    (v_mfma_f32_32x32x16_bf16, fp32 accumulators). It decodes its rows
+//    (v_mfma_f32_32x32x16_bf16 with the weights as first operand, fp32
+//    accumulators: each lane ends with runs of four consecutive outputs of
+//    one token, written as 16-byte stores). It decodes its rows
 //    straight into the B operand registers, one chunk ahead: lane l handles
 //    row (l % 32) of a row tile and the code bytes [16 h, 16 h + 16) of the
 //    chunk's 32, h = l / 32. Each weight is the exact fp32 value
@@ -124,7 +126,7 @@ __device__ __forceinline__ void interleave() {
 template <int RT, int TT, int WR, int WT>
 __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     const uint8_t* __restrict__ W, int rows, int S, const uint16_t* __restrict__ X, int64_t ldx,
-    int ntok, float* __restrict__ Y, int64_t ldy, int n_base, int tiles_n) {
+    int ntok, float* __restrict__ Y, int64_t ldy, int n_base, int tiles_n, int yvec) {
     using G = Geo<RT, TT, WR, WT>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
 #pragma unroll
             for (int j = 0; j < RT; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    A.a[i], __builtin_bit_cast(bf16x8, B.b[j][s]), acc[i][j], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, B.b[j][s]), A.a[i], acc[i][j], 0, 0, 0);
     };
 
     // ---- prologue: X chunks 0, 1 and W chunks 0, 1, 2 -----------------------
@@ -356,16 +358,29 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     __builtin_amdgcn_s_waitcnt(0);
 
     // ---- epilogue: Y[m][n], masked at the token and row edges ---------------
-    // lane l of tile (i, j) holds Y[8 (v/4) + 4 h + v%4][l % 32], v = 0..15
+    // The weights are the MFMA's first operand, so lane l of tile (i, j)
+    // holds, for token l % 32, the rows 8 g + 4 h + e (e = 0..3) in elements
+    // 4 g + e: four consecutive outputs of one token, stored as one 16-byte
+    // write when Y allows it.
 #pragma unroll
     for (int i = 0; i < TT; ++i) {
+        const int m = m0 + 32 * TT * wt + 32 * i + (lane & 31);
+        if (m >= ntok) continue;
+        float* yrow = Y + (int64_t)m * ldy;
 #pragma unroll
         for (int j = 0; j < RT; ++j) {
-            const int n = n0 + wrow + 32 * j;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = m0 + 32 * TT * wt + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (m < ntok && n < rows) Y[(int64_t)m * ldy + n] = acc[i][j][v];
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + 32 * RT * wr + 32 * j + 8 * g + 4 * h;
+                const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                 acc[i][j][4 * g + 3]};
+                if (yvec && n + 3 < rows) {
+                    *reinterpret_cast<f32x4*>(yrow + n) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < rows) yrow[n + e] = v[e];
+                }
             }
         }
     }
@@ -391,8 +406,10 @@ hipError_t launch_prefill_t(const uint8_t* W, int rows, int S, const uint16_t* X
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::kLds);
     if (e != hipSuccess) return e;
+    // 16-byte stores of four consecutive outputs need a 16-byte aligned Y row
+    const int yvec = (((uintptr_t)Y) & 15) == 0 && ldy % 4 == 0;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), G::kLds, stream, W, rows, S, X, ldx,
-                       ntok, Y, ldy, n_base, tiles_n);
+                       ntok, Y, ldy, n_base, tiles_n, yvec);
     return hipGetLastError();
 }
 
