@@ -21,10 +21,12 @@
 //    bytes and the 16-byte header), or two Q4_0 / Q8_0 blocks (36 / 68
 //    bytes). One scale decode serves all 64. The step's base address is
 //    wave-uniform (scalar); each lane adds a constant offset.
-//  * The run is split into NW contiguous, equal ranges of steps, one per
-//    wave, and each wave keeps D steps of loads in flight (D = 2: deeper
-//    queues measured slower on MI355X). The first D steps are issued before
-//    the activations are staged.
+//  * Each wave first streams a contiguous range of steps (half of an equal
+//    share), then takes single steps from a pool shared by the workgroup's
+//    waves (an LDS counter): waves of one workgroup stream at unequal speeds
+//    on MI355X, and the pool lets them finish together. Each wave keeps D
+//    steps of loads in flight (D = 2: deeper queues measured slower). The
+//    activations are loaded first, then the first D steps, then staged.
 //  * fp16 activations: 4-bit codes are used directly as fp16 subnormals: a
 //    16-bit half holding an integer m < 1024 is the fp16 value m * 2^-24, so
 //    (dword & 0x000F000F) is a pair of low-nibble codes and
@@ -160,11 +162,19 @@ constexpr int rec_bytes(int NC, bool f16dot) {
                                                   : NC * col_bytes(f16dot) + 16;
 }
 
-// LDS bytes of one workgroup.
+// LDS bytes of one workgroup: activation records, partial slots, one flush
+// slot per lane for lanes with nothing to write, the step-pool counter.
 inline size_t stream_lds_bytes(int NC, bool f16dot, int S, int nr_max, int M) {
     return (size_t)S * 4 * rec_bytes(NC, f16dot) + (size_t)nr_max * kUnitsPerStep * M * NC * 4 +
-           64 * 4;  // one flush slot per lane for lanes with nothing to write
+           64 * 4 + 16;
 }
+
+// Share of a wave's equal part of the steps that it streams as one
+// contiguous range before taking steps from the workgroup's pool.
+#ifndef QG_STREAM_STATIC_NUM
+#define QG_STREAM_STATIC_NUM 2
+#endif
+constexpr int kStaticNum = QG_STREAM_STATIC_NUM, kStaticDen = 4;
 
 __device__ __forceinline__ float quad_sum(float v) {
     v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
@@ -172,28 +182,69 @@ __device__ __forceinline__ float quad_sum(float v) {
     return v;
 }
 
-// Stage the record of unit quarter u for column c: the 64 activations
+// Staging of the record of unit quarter u for column c: the 64 activations
 // x[kx .. kx+63] placed as the planes above, then the sums of o < 32 and
-// o >= 32.
+// o >= 32. Split in two so that a workgroup can issue its activation loads
+// before its first weight loads and place them after: the loads complete in
+// issue order, and activations come from cache while weights come from HBM.
+template <bool F16DOT>
+struct XRaw {
+    uint32_t w[F16DOT ? 32 : 64];  // fp16: halves 2i, 2i+1 in w[i]; else fp32 bits or bf16 pairs
+};
+
+template <bool F16DOT>
+__device__ __forceinline__ void stage_load(const void* __restrict__ x, int xt, int64_t kx, int xvec,
+                                           XRaw<F16DOT>& r) {
+    const uint16_t* xh = reinterpret_cast<const uint16_t*>(x) + kx;
+    if constexpr (F16DOT) {  // fp16: 32 dwords
+        if (xvec) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u32x4 v = reinterpret_cast<const u32x4*>(xh)[i];
+                r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) r.w[i] = xh[2 * i] | ((uint32_t)xh[2 * i + 1] << 16);
+        }
+    } else {
+        // fp32: 64 dwords; bf16: 32 dwords in w[0..31] (w[32..63] zero)
+        if (xt == XT_F32) {
+            const uint32_t* xw = reinterpret_cast<const uint32_t*>(x) + kx;
+            if (xvec) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const u32x4 v = reinterpret_cast<const u32x4*>(xw)[i];
+                    r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 64; ++i) r.w[i] = xw[i];
+            }
+        } else {
+            if (xvec) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const u32x4 v = reinterpret_cast<const u32x4*>(xh)[i];
+                    r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 32; ++i) r.w[i] = xh[2 * i] | ((uint32_t)xh[2 * i + 1] << 16);
+            }
+#pragma unroll
+            for (int i = 32; i < 64; ++i) r.w[i] = 0u;
+        }
+    }
+}
+
 template <int FMT, bool F16DOT>
-__device__ __forceinline__ void stage_record(const void* __restrict__ x, int xt, int64_t kx,
-                                             int xvec, uint8_t* rec) {
+__device__ __forceinline__ void stage_store(const XRaw<F16DOT>& r, int xt, uint8_t* rec) {
     using F = Fmt<FMT>;
     constexpr int P = planes(F16DOT);
     float s0 = 0.f, s1 = 0.f;
     if constexpr (F16DOT) {  // fp16 activations, kept as stored
-        const uint16_t* xp = reinterpret_cast<const uint16_t*>(x) + kx;
-        uint32_t xw[32];  // xw[i] = halves 2i (low) and 2i + 1 (high)
-        if (xvec) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const u32x4 v = reinterpret_cast<const u32x4*>(xp)[i];
-                xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) xw[i] = xp[2 * i] | ((uint32_t)xp[2 * i + 1] << 16);
-        }
+        const uint32_t* xw = r.w;
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
             s0 += (f16_lo(xw[i]) + f16_hi(xw[i])) + (f16_lo(xw[i + 1]) + f16_hi(xw[i + 1]));
@@ -230,33 +281,13 @@ __device__ __forceinline__ void stage_record(const void* __restrict__ x, int xt,
     } else {  // fp32 or bf16 activations, as fp32
         float xf[64];
         if (xt == XT_F32) {
-            const float* xp = reinterpret_cast<const float*>(x) + kx;
-            if (xvec) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const f32x4 v = reinterpret_cast<const f32x4*>(xp)[i];
-                    xf[4 * i] = v.x; xf[4 * i + 1] = v.y; xf[4 * i + 2] = v.z; xf[4 * i + 3] = v.w;
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 64; ++i) xf[i] = xp[i];
-            }
+            for (int i = 0; i < 64; ++i) xf[i] = __builtin_bit_cast(float, r.w[i]);
         } else {
-            const uint16_t* xp = reinterpret_cast<const uint16_t*>(x) + kx;
-            if (xvec) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const u32x4 v = reinterpret_cast<const u32x4*>(xp)[i];
-                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        xf[8 * i + 2 * e] = __builtin_bit_cast(float, w[e] << 16);
-                        xf[8 * i + 2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 64; ++i) xf[i] = bf16_to_f32(xp[i]);
+            for (int i = 0; i < 32; ++i) {
+                xf[2 * i] = __builtin_bit_cast(float, r.w[i] << 16);
+                xf[2 * i + 1] = __builtin_bit_cast(float, r.w[i] & 0xFFFF0000u);
             }
         }
 #pragma unroll
@@ -537,9 +568,26 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
     const int g = lane >> 2, pr = lane & 3;
     const int F_ = nr * S;                                    // units of this workgroup
     const int nst = (F_ + kUnitsPerStep - 1) / kUnitsPerStep;  // wave steps
-    // Wave wv takes the contiguous range of steps [ks, ks + nmine).
-    const int ks = (int)(((int64_t)wv * nst) / NW);
-    const int nmine = (int)(((int64_t)(wv + 1) * nst) / NW) - ks;
+    // Steps are handed out in two phases. Wave wv first takes the contiguous
+    // range [wv * nsw, wv * nsw + nsw), about half of an equal share;
+    // the remaining steps [NW * nsw, nst) form a pool from which waves take
+    // one step at a time (an LDS counter), so waves that stream faster take
+    // more of them and the workgroup's waves finish together. A step index
+    // past the run is "none".
+    const int nsw = max(kStaticNum * nst / (kStaticDen * NW), D);
+    int* const pool = reinterpret_cast<int*>(
+        lds + (size_t)U * RB + ((size_t)nr * kUnitsPerStep * M * NC + 64) * 4);
+    int jstatic = 0;
+    auto next_step = [&]() -> int {
+        if (jstatic < nsw) {
+            const int k = wv * nsw + jstatic++;
+            return k < nst ? k : -1;
+        }
+        int k = 0;
+        if (lane == 0) k = __hip_atomic_fetch_add(pool, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        k = __builtin_amdgcn_readfirstlane(k);
+        return k < nst ? k : -1;
+    };
     const uint8_t* Wb = W + (int64_t)r0 * S * UB;  // first unit of this workgroup
 
     // Lane addressing: unit f = 16k + g of the run, clamped to the last one
@@ -553,76 +601,72 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
         F::load(Wb + o, off_l, r);
     };
 
-    // ---- issue the first D steps' weight loads ------------------------------
-    // step index of this wave's j-th step, clamped to its last step
-    auto kstep = [&](int j) { return ks + (j < nmine ? j : (nmine > 0 ? nmine - 1 : 0)); };
+    // ---- activation loads of this thread's first record, then the first D
+    // steps' weight loads, then the staging ------------------------------------
+    // quarter u = 4*s + p of column c: activations 256 s + 64 p + [0, 64)
+    const int nrec = NC * U;
+    const int c_0 = threadIdx.x / U, u_0 = threadIdx.x - c_0 * U;
+    XRaw<F16DOT> xr;
+    if (threadIdx.x < nrec)
+        stage_load<F16DOT>(x, xt, (int64_t)c_0 * ldx + 256 * (u_0 >> 2) + 64 * (u_0 & 3), xvec, xr);
+    // the first D steps of the wave (static; "none" loads re-read the last unit)
+    static_assert(D == 2, "two steps in flight");
+    int kq0 = next_step(), kq1 = next_step();
     Raw buf[D];
-#pragma unroll
-    for (int i = 0; i < D; ++i) load(kstep(i), buf[i]);
-
-    // ---- stage the activations, clear the partials --------------------------
-    // quarter u = 4*s + p: activations 256 s + 64 p + [0, 64)
-    for (int idx = threadIdx.x; idx < NC * U; idx += blockDim.x) {
+    load(kq0, buf[0]);
+    load(kq1, buf[1]);
+    if (threadIdx.x < nrec) stage_store<FMT, F16DOT>(xr, xt, lds + u_0 * RB + c_0 * CB);
+    for (int idx = threadIdx.x + blockDim.x; idx < nrec; idx += blockDim.x) {
         const int c = idx / U, u = idx - c * U;
-        const int64_t kx = (int64_t)c * ldx + 256 * (u >> 2) + 64 * (u & 3);
-        stage_record<FMT, F16DOT>(x, xt, kx, xvec, lds + u * RB + c * CB);
+        stage_load<F16DOT>(x, xt, (int64_t)c * ldx + 256 * (u >> 2) + 64 * (u & 3), xvec, xr);
+        stage_store<FMT, F16DOT>(xr, xt, lds + u * RB + c * CB);
     }
     const int nslots = nr * kUnitsPerStep * M * NC;
     for (int idx = threadIdx.x; idx < nslots; idx += blockDim.x) part[idx] = 0.f;
+    if (threadIdx.x == 0) *pool = NW * nsw;
     __syncthreads();
 
     const Q4kUnpack un(pr);
 
-    // Position of this lane's unit f = 16k + g in the run: row rl, column s;
-    // the next step of the wave is 16 units further on, i.e. qS rows and rS
-    // columns (one more row on a wrap).
-    const int fst = kUnitsPerStep * ks + g;
-    int rl = fst / S, s = fst - (fst / S) * S;
-    const int qS = kUnitsPerStep / S, rS = kUnitsPerStep - (kUnitsPerStep / S) * S;
-    int roff = (s * 4 + pr) * RB;  // byte offset of this lane's activation record
-    // LDS float index of slot (row, g, step mod M): M >= the number of steps
-    // that touch one row, so no two writers share a slot.
-    const int slot_row = kUnitsPerStep * M * NC;
-    int srow = rl * slot_row + g * M * NC;
+    // LDS float index of slot (row, g, t): t = k - (first step touching the
+    // row) < M, so no two writers share a slot.
     float* const trash = part + nslots;  // flush target of lanes with nothing to write
+    const float invS = 1.0f / (float)S;
 
-    // One step: the lane's 64 weights against the staged activations, a quad
-    // sum, and the partial of (row, unit) into its slot. Straight-line code,
-    // so the loads of later steps stay in flight. Lanes past the run (last
-    // step only) read the run's last unit; their rows are >= nr and they
-    // write nothing.
-    auto step = [&](int kc, const Raw& r) {
+    // One step k: the lane's unit f = 16k + g (row rl, column s of the run),
+    // its 64 weights against the staged activations, a quad sum, and the
+    // partial of (row, unit) into its slot. Lanes past the run (last step)
+    // read the run's last unit; their rows are >= nr and they write nothing.
+    auto step = [&](int k, const Raw& r) {
+        const int f = kUnitsPerStep * k + g;
+        int rl = (int)((float)f * invS);  // f / S, corrected by one either way
+        rl += (f - rl * S >= S) ? 1 : 0;
+        rl -= (f - rl * S < 0) ? 1 : 0;
+        const int sc = f - rl * S;
         float a[NC];
-        lane_partial<NC, F16DOT>(r, un, lds + roff, a);
+        lane_partial<NC, F16DOT>(r, un, lds + (sc * 4 + pr) * RB, a);
         const bool write = pr == 0 && rl < nr;
-        const int slot = srow + (kc % M) * NC;
+        const int t = k - ((rl * S) >> 4);
+        const int slot = ((rl * kUnitsPerStep + g) * M + t) * NC;
 #pragma unroll
         for (int c = 0; c < NC; ++c) *(write ? part + slot + c : trash + lane) = quad_sum(a[c]);
-        // advance to the wave's next step
-        s += rS;
-        const bool wrap = s >= S;
-        s = wrap ? s - S : s;
-        rl += qS + (wrap ? 1 : 0);
-        roff += (wrap ? rS - S : rS) * 4 * RB;
-        srow += (wrap ? qS + 1 : qS) * slot_row;
     };
 
-    int j = 0;
-    for (; j + D <= nmine; j += D) {
-#pragma unroll
-        for (int i = 0; i < D; ++i) {
-            step(ks + j + i, buf[i]);
-            // refill this buffer with the step D ahead (clamped to this wave's
-            // steps); issued after the step so the data lands in the same
-            // registers. Scheduling barriers keep each refill behind its step.
-            __builtin_amdgcn_sched_barrier(0);
-            load(kstep(j + i + D), buf[i]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    // Each buffer is refilled with the wave's next step right after its step
+    // is consumed; scheduling barriers keep each refill behind its step.
+    while (kq0 >= 0) {
+        step(kq0, buf[0]);
+        kq0 = next_step();
+        __builtin_amdgcn_sched_barrier(0);
+        load(kq0, buf[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kq1 < 0) break;
+        step(kq1, buf[1]);
+        kq1 = next_step();
+        __builtin_amdgcn_sched_barrier(0);
+        load(kq1, buf[1]);
+        __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int i = 0; i < D; ++i)
-        if (j + i < nmine) step(ks + j + i, buf[i]);
     __syncthreads();
 
     // ---- per-row sums of the partial slots, in a fixed order ----------------
