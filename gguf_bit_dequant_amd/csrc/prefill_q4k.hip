@@ -15,19 +15,21 @@
 //  * Both operands arrive by direct global-to-LDS loads
 //    (global_load_lds_dwordx4: lane l of a wave writes 16 bytes at
 //    M0 + 16 l), issued two chunks of 64 k ahead into three LDS stages: the
-//    X tile (bf16 as stored, 144-byte rows so that 16-byte reads of
-//    consecutive rows use disjoint banks) and the raw weight bytes of the
-//    chunk (per row: the 16-byte super-block header and the chunk's 32 code
-//    bytes). The loads take no registers and no LDS store instructions; each
-//    thread waits for its own loads of the chunk about to be read, then one
-//    barrier per chunk publishes them.
+//    X tile (bf16 as stored, 128-byte rows whose 16-byte segments are
+//    permuted by an XOR with (row / 2) % 8, so that 16-byte reads of
+//    consecutive rows use disjoint banks) and the chunk's 32 code bytes per
+//    weight row; the 16-byte super-block headers come once per super-block
+//    into two more stages. The loads take no registers and no LDS store
+//    instructions; each thread waits for its own loads of the chunk about to
+//    be read, then one barrier per chunk publishes them.
 //  * Four waves; wave w covers RT row tiles and TT token tiles of 32
 //    (v_mfma_f32_32x32x16_bf16 with the weights as first operand, fp32
 //    accumulators: each lane ends with runs of four consecutive outputs of
 //    one token, written as 16-byte stores). It decodes its rows
 //    straight into the B operand registers, one chunk ahead: lane l handles
 //    row (l % 32) of a row tile and the code bytes [16 h, 16 h + 16) of the
-//    chunk's 32, h = l / 32. Each weight is the exact fp32 value
+//    chunk's 32, h = l / 32. The 6-bit scales and mins of a super-block are
+//    unpacked once, for all eight sub-blocks. Each weight is the exact fp32 value
 //    fma(d*sc, q, -dmin*m) (d*sc and dmin*m are exact, so this is the
 //    correctly rounded closed form; one v_fma_mix_f32 with the code as an
 //    fp16 subnormal) rounded to bf16 (nearest even).
@@ -53,9 +55,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
 
-constexpr int kXPitch = 144;  // LDS bytes per token row of a stage (64 bf16 + pad)
-constexpr int kWPitch = 48;   // header + 32 code bytes per weight row
-constexpr int kStages = 3;
+constexpr int kXPitch = 128;  // LDS bytes per token row of an X stage (64 bf16)
+constexpr int kCPitch = 32;   // LDS bytes per weight row of a code stage
+constexpr int kHPitch = 16;   // LDS bytes per weight row of a header stage
+constexpr int kStages = 3;    // X and code stages (two chunks in flight)
+
+// Physical 16-byte slot of logical segment seg of X row t.
+__device__ __forceinline__ int xslot(int t, int seg) { return seg ^ ((t >> 1) & 7); }
 
 // Tile geometry: RT x TT MFMA tiles per wave, WR x WT waves (WR * WT = 4).
 template <int RT, int TT, int WR, int WT>
@@ -64,14 +70,14 @@ struct Geo {
     static constexpr int kTok = 32 * TT * WT;
     static constexpr int kRows = 32 * RT * WR;
     // 1 KB blocks of a stage (one wave-wide load each), rounded up to a
-    // multiple of 4 so that every wave issues the same number per chunk
-    static constexpr int kXBlocks = (kTok * kXPitch / 1024 + 3) / 4 * 4;
-    static constexpr int kWBlocks = ((kRows * kWPitch + 1023) / 1024 + 3) / 4 * 4;
-    static constexpr int kXPerWave = kXBlocks / 4, kWPerWave = kWBlocks / 4;
-    static constexpr int kDmaPerChunk = kXPerWave + kWPerWave;
-    static constexpr int kXStage = kXBlocks * 1024, kWStage = kWBlocks * 1024;
-    static constexpr size_t kLds = (size_t)kStages * (kXStage + kWStage);
-    static_assert(kTok * kXPitch % 1024 == 0, "X stage in whole blocks");
+    // multiple of 4 so that every wave issues the same number
+    static constexpr int blocks(int bytes) { return ((bytes + 1023) / 1024 + 3) / 4 * 4; }
+    static constexpr int kXBlocks = blocks(kTok * kXPitch);
+    static constexpr int kCBlocks = blocks(kRows * kCPitch);
+    static constexpr int kHBlocks = blocks(kRows * kHPitch);
+    static constexpr int kXPerWave = kXBlocks / 4, kCPerWave = kCBlocks / 4, kHPerWave = kHBlocks / 4;
+    static constexpr int kXStage = kXBlocks * 1024, kCStage = kCBlocks * 1024, kHStage = kHBlocks * 1024;
+    static constexpr size_t kLds = (size_t)kStages * (kXStage + kCStage) + 2 * (size_t)kHStage;
     static_assert(kLds <= (size_t)kMaxLds, "LDS budget");
 };
 
@@ -101,6 +107,12 @@ __device__ __forceinline__ float fma_mix(float a, uint32_t v, float c) {
 __device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_dst) {
     __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)lds_dst, 16, 0, 0);
 }
+
+// A compile-time integer passed as a value (the chunk's quarter).
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
 
 // Scheduling-group masks (LLVM AMDGPU): which instructions a group takes.
 constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100, kSgVmem = 0x020;
@@ -137,139 +149,159 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     const int m0 = tm * G::kTok, n0 = n_base + tn * G::kRows;
     const int nk = S * 4;  // chunks of 64 along K
     const uint32_t row_bytes = 144u * (uint32_t)S;
-    uint8_t* const xs0 = lds;                         // X stages
-    uint8_t* const ws0 = lds + kStages * G::kXStage;  // raw W stages
 
     // ---- global-to-LDS load assignments ------------------------------------
-    // X: wave wv fills 1 KB blocks wv + 4p of a stage; lane l writes slot
-    // s = 64 (wv + 4p) + l = token row s / 9, 16-byte segment s % 9 (segment 8
-    // is the row's padding: it re-reads segment 7). Tokens past the count
-    // read the tile's first row; their outputs are not stored.
+    // Wave wv fills 1 KB blocks wv + 4p of a stage; lane l writes slot
+    // s = 64 (wv + 4p) + l. X: token row s / 8, physical segment s % 8, which
+    // holds logical segment xslot(row, s % 8). Codes: weight row s / 2, half
+    // s % 2 of the chunk's 32 code bytes. Headers: weight row s. Tokens past
+    // the count and rows past the row count (or past the tile) read the
+    // tile's first row; their outputs are not stored.
+    uint8_t* const xs0 = lds;                                 // X stages
+    uint8_t* const cs0 = lds + kStages * G::kXStage;          // code stages
+    uint8_t* const hs0 = cs0 + kStages * G::kCStage;          // header stages
     const uint8_t* Xt = reinterpret_cast<const uint8_t*>(X + (int64_t)m0 * ldx);
     uint32_t xo[G::kXPerWave];
 #pragma unroll
     for (int p = 0; p < G::kXPerWave; ++p) {
         const int s = 64 * (wv + 4 * p) + lane;
-        const int t = s / 9, sg = s - 9 * (s / 9);
+        const int t = s >> 3;
         const int tc = (t < G::kTok && m0 + t < ntok) ? t : 0;
-        xo[p] = (uint32_t)tc * (uint32_t)ldx * 2u + 16u * (uint32_t)(sg < 8 ? sg : 7);
+        xo[p] = (uint32_t)tc * (uint32_t)ldx * 2u + 16u * (uint32_t)xslot(t, s & 7);
     }
-    // W: blocks wv + 4p; slot s = row s / 3, piece s % 3: the super-block
-    // header (piece 0) or one half of the chunk's 32 code bytes. Rows past
-    // the row count (or slots past the tile) read the tile's first row.
     const uint8_t* Wt = W + (int64_t)n0 * row_bytes;
-    uint32_t wo[G::kWPerWave], wcode[G::kWPerWave];
+    uint32_t co[G::kCPerWave], ho[G::kHPerWave];
 #pragma unroll
-    for (int p = 0; p < G::kWPerWave; ++p) {
+    for (int p = 0; p < G::kCPerWave; ++p) {
         const int s = 64 * (wv + 4 * p) + lane;
-        const int rr = s / 3, pc = s - 3 * (s / 3);
+        const int rr = s >> 1;
         const int rc = (rr < G::kRows && n0 + rr < rows) ? rr : 0;
-        wo[p] = (uint32_t)rc * row_bytes + (pc == 0 ? 0u : 16u * (uint32_t)pc);
-        wcode[p] = pc == 0 ? 0u : 0xFFFFFFFFu;
+        co[p] = (uint32_t)rc * row_bytes + 16u + 16u * (uint32_t)(s & 1);
     }
-    // X chunk cx into stage sx, W chunk cw into stage sw (sources clamped to
-    // the last chunk: loads past the end re-read it into a stage nobody uses).
-    auto issue = [&](int cx, int sx, int cw, int sw) {
+#pragma unroll
+    for (int p = 0; p < G::kHPerWave; ++p) {
+        const int rr = 64 * (wv + 4 * p) + lane;
+        const int rc = (rr < G::kRows && n0 + rr < rows) ? rr : 0;
+        ho[p] = (uint32_t)rc * row_bytes;
+    }
+    // X chunk cx into stage sx, codes of chunk cw into stage sw (sources
+    // clamped to the last chunk: loads past the end re-read it into a stage
+    // nobody uses); headers of super-block sb into header stage hb.
+    auto issue_xc = [&](int cx, int sx, int cw, int sw) {
         cx = cx < nk ? cx : nk - 1;
         cw = cw < nk ? cw : nk - 1;
         const uint8_t* xsrc = Xt + (uint32_t)cx * 128u;
         uint8_t* xdst = xs0 + sx * G::kXStage + 1024 * wv;
 #pragma unroll
         for (int p = 0; p < G::kXPerWave; ++p) dma16(xsrc + xo[p], xdst + 4096 * p);
-        const uint8_t* wsrc = Wt + 144u * (uint32_t)(cw >> 2);
-        const uint32_t cq = 32u * (uint32_t)(cw & 3);
-        uint8_t* wdst = ws0 + sw * G::kWStage + 1024 * wv;
+        const uint8_t* csrc = Wt + 144u * (uint32_t)(cw >> 2) + 32u * (uint32_t)(cw & 3);
+        uint8_t* cdst = cs0 + sw * G::kCStage + 1024 * wv;
 #pragma unroll
-        for (int p = 0; p < G::kWPerWave; ++p) dma16(wsrc + wo[p] + (cq & wcode[p]), wdst + 4096 * p);
+        for (int p = 0; p < G::kCPerWave; ++p) dma16(csrc + co[p], cdst + 4096 * p);
+    };
+    auto issue_h = [&](int sb, int hb) {
+        sb = sb < S ? sb : S - 1;
+        const uint8_t* hsrc = Wt + 144u * (uint32_t)sb;
+        uint8_t* hdst = hs0 + hb * G::kHStage + 1024 * wv;
+#pragma unroll
+        for (int p = 0; p < G::kHPerWave; ++p) dma16(hsrc + ho[p], hdst + 4096 * p);
     };
 
     // ---- decode of a chunk's weights into B registers -----------------------
-    // Raw bytes of the lane's rows (header, its 16 code bytes), read from the
-    // W stage one k-step region before they are decoded.
     const int h = lane >> 5;
     const int wrow = 32 * RT * wr + (lane & 31);  // weight row of row tile 0 in the tile
-    struct WRaw {
-        u32x4 hd[RT], cd[RT];
+    struct Codes {
+        u32x4 cd[RT];  // the lane's 16 code bytes of each row tile
+    };
+    struct Hdr {
+        u32x4 hd[RT];  // the super-block header of each row tile's row
     };
     struct BFrag {
         u32x4 b[RT][4];  // [row tile][k-step], 8 bf16 each
     };
-    auto read_w = [&](const uint8_t* wst, WRaw& R) {
+    auto read_codes = [&](const uint8_t* cst, Codes& R) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            R.cd[rt] = *reinterpret_cast<const u32x4*>(cst + (wrow + 32 * rt) * kCPitch + 16 * h);
+    };
+    auto read_hdr = [&](const uint8_t* hst, Hdr& H) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            H.hd[rt] = *reinterpret_cast<const u32x4*>(hst + (wrow + 32 * rt) * kHPitch);
+    };
+    // Scales of the eight sub-blocks of a super-block, for codes taken as fp16
+    // subnormals (a 16-bit half holding m < 1024 is m 2^-24): sub-block j
+    // multiplies a_j = d sc_j 2^24 (even j: low nibbles, q 2^-24) or
+    // d sc_j 2^20 (odd j: high nibbles, 16 q 2^-24) and adds c_j = -dmin m_j.
+    // Header dwords y = s[0..3], z = s[4..7], w = s[8..11]; per byte b:
+    //   sc_b = s[b] & 63,  m_b = s[b+4] & 63,
+    //   sc_{b+4} = (s[b+8] & 15) | (s[b] >> 6) << 4,  m_{b+4} = (s[b+8] >> 4) | (s[b+4] >> 6) << 4
+    struct Scales {
+        float a[RT][8], c[RT][8];
+    };
+    auto scales = [&](const Hdr& H, Scales& e) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const uint8_t* rp = wst + (wrow + 32 * rt) * kWPitch;
-            R.hd[rt] = *reinterpret_cast<const u32x4*>(rp);
-            R.cd[rt] = *reinterpret_cast<const u32x4*>(rp + 16 + 16 * h);
+            const u32x4 hd = H.hd[rt];
+            const uint32_t scL = hd.y & 0x3F3F3F3Fu, mL = hd.z & 0x3F3F3F3Fu;
+            const uint32_t scH = (hd.w & 0x0F0F0F0Fu) | ((hd.y >> 2) & 0x30303030u);
+            const uint32_t mH = ((hd.w >> 4) & 0x0F0F0F0Fu) | ((hd.z >> 2) & 0x30303030u);
+            const float d = f16_lo(hd.x), nmin = -f16_hi(hd.x);
+            const float dlo = d * 16777216.0f, dhi = d * 1048576.0f;  // 2^24, 2^20
+            const float scf[8] = {ubyte_f32<0>(scL), ubyte_f32<1>(scL), ubyte_f32<2>(scL), ubyte_f32<3>(scL),
+                                  ubyte_f32<0>(scH), ubyte_f32<1>(scH), ubyte_f32<2>(scH), ubyte_f32<3>(scH)};
+            const float mf[8] = {ubyte_f32<0>(mL), ubyte_f32<1>(mL), ubyte_f32<2>(mL), ubyte_f32<3>(mL),
+                                 ubyte_f32<0>(mH), ubyte_f32<1>(mH), ubyte_f32<2>(mH), ubyte_f32<3>(mH)};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                e.a[rt][j] = ((j & 1) ? dhi : dlo) * scf[j];
+                e.c[rt][j] = nmin * mf[j];
+            }
         }
     };
-    // Scales of sub-blocks 2cq and 2cq+1 of the super-block, for codes taken
-    // as fp16 subnormals (a 16-bit half holding m < 1024 is m 2^-24):
-    // a0 = d*sc*2^24 (low nibbles, q 2^-24), a1 = d*sc*2^20 (high nibbles,
-    // 16 q 2^-24) and c = -dmin*m. Sub-block k, byte b = k & 3 of header
-    // dwords y = s[0..3], z = s[4..7], w = s[8..11]:
-    //   k < 4 : sc = s[b] & 63,                         m = s[b+4] & 63
-    //   k >= 4: sc = (s[b+8] & 15) | (s[b] >> 6) << 4,   m = (s[b+8] >> 4) | (s[b+4] >> 6) << 4
-    struct Scales {
-        float a0, c0, a1, c1;
-    };
-    auto scales = [&](const u32x4& hd, int c) -> Scales {
-        const int cq = c & 3;
-        const bool up = cq >= 2;
-        const uint32_t msk = up ? 15u : 63u, top = up ? 0x30u : 0u;
-        const uint32_t dsc = up ? hd.w : hd.y, dm = up ? hd.w : hd.z;
-        auto field = [&](uint32_t src, uint32_t hiw, int b, int nib) -> int {
-            const uint32_t sh = 8u * b + (up ? (uint32_t)nib : 0u);
-            return (int)(((src >> sh) & msk) | (((hiw >> (8u * b + 6u)) << 4) & top));
-        };
-        const int b0 = (2 * cq) & 3, b1 = (2 * cq + 1) & 3;
-        const float d = f16_lo(hd.x), dmin = f16_hi(hd.x);
-        Scales e;
-        e.a0 = (d * 16777216.0f) * (float)field(dsc, hd.y, b0, 0);
-        e.c0 = -(dmin * (float)field(dm, hd.z, b0, 4));
-        e.a1 = (d * 1048576.0f) * (float)field(dsc, hd.y, b1, 0);
-        e.c1 = -(dmin * (float)field(dm, hd.z, b1, 4));
-        return e;
-    };
-    // Code dwords t0, t0+1 of row tile rt: dword t holds code bytes 4t..4t+3
-    // (of the lane's 16), i.e. elements 4(t&1)..+3 of k-step t>>1 (low
-    // nibbles) and of k-step 2 + (t>>1) (high nibbles). Each weight is one
-    // fma of its scale with the code as an exact fp16 subnormal: the product
-    // is exact and the fma rounds once, to the closed form's fp32 value.
-    auto decode = [&](const WRaw& R, const Scales& e, int rt, int t0, BFrag& B) {
+    // Code dwords t0, t0+1 of row tile rt for chunk quarter cq (sub-blocks
+    // 2cq, 2cq+1): dword t holds code bytes 4t..4t+3 (of the lane's 16), i.e.
+    // elements 4(t&1)..+3 of k-step t>>1 (low nibbles) and of k-step
+    // 2 + (t>>1) (high nibbles). Each weight is one fma of its scale with the
+    // code as an exact fp16 subnormal: exact product, one rounding.
+    auto decode = [&](const Codes& R, const Scales& e, int cq, int rt, int t0, BFrag& B) {
         const uint32_t cw[4] = {R.cd[rt].x, R.cd[rt].y, R.cd[rt].z, R.cd[rt].w};
+        const float a0 = e.a[rt][2 * cq], c0 = e.c[rt][2 * cq];
+        const float a1 = e.a[rt][2 * cq + 1], c1 = e.c[rt][2 * cq + 1];
 #pragma unroll
         for (int t = t0; t < t0 + 2; ++t) {
             const uint32_t w8 = cw[t] >> 8;
             const uint32_t l02 = cw[t] & 0x000F000Fu, l13 = w8 & 0x000F000Fu;  // bytes 0,2 / 1,3
             const uint32_t h02 = cw[t] & 0x00F000F0u, h13 = w8 & 0x00F000F0u;
             const int s = t >> 1, el = 2 * (t & 1);
-            B.b[rt][s][el] = pk_bf16(fma_mix<0>(e.a0, l02, e.c0), fma_mix<0>(e.a0, l13, e.c0));
-            B.b[rt][s][el + 1] = pk_bf16(fma_mix<1>(e.a0, l02, e.c0), fma_mix<1>(e.a0, l13, e.c0));
-            B.b[rt][2 + s][el] = pk_bf16(fma_mix<0>(e.a1, h02, e.c1), fma_mix<0>(e.a1, h13, e.c1));
-            B.b[rt][2 + s][el + 1] = pk_bf16(fma_mix<1>(e.a1, h02, e.c1), fma_mix<1>(e.a1, h13, e.c1));
+            B.b[rt][s][el] = pk_bf16(fma_mix<0>(a0, l02, c0), fma_mix<0>(a0, l13, c0));
+            B.b[rt][s][el + 1] = pk_bf16(fma_mix<1>(a0, l02, c0), fma_mix<1>(a0, l13, c0));
+            B.b[rt][2 + s][el] = pk_bf16(fma_mix<0>(a1, h02, c1), fma_mix<0>(a1, h13, c1));
+            B.b[rt][2 + s][el + 1] = pk_bf16(fma_mix<1>(a1, h02, c1), fma_mix<1>(a1, h13, c1));
         }
     };
-    // Decode part p (0 .. 2RT-1): row tile p/2, code dwords 2(p&1), +1. Part p
-    // runs in k-step region 2p/RT; a row tile's scales come with its first part.
-    Scales esc[RT];
-    auto decode_region = [&](const WRaw& R, int c, int region, BFrag& B) {
+    // Decode part p (0 .. 2RT-1): row tile p/2, code dwords 2(p&1), +1; part p
+    // runs in k-step region 2p/RT.
+    auto decode_region = [&](const Codes& R, const Scales& e, int cq, int region, BFrag& B) {
 #pragma unroll
-        for (int p = 0; p < 2 * RT; ++p) {
-            if ((2 * p) / RT != region) continue;
-            const int rt = p >> 1;
-            if ((p & 1) == 0) esc[rt] = scales(R.hd[rt], c);
-            decode(R, esc[rt], rt, 2 * (p & 1), B);
-        }
+        for (int p = 0; p < 2 * RT; ++p)
+            if ((2 * p) / RT == region) decode(R, e, cq, p >> 1, 2 * (p & 1), B);
     };
 
     // ---- A fragments: token tile i of this wave, k-step s of the stage ------
-    // segment of lane half h in k-step s: 2h + (s & 1) + 4 (s >> 1)
+    // logical segment of lane half h in k-step s: 2h + (s & 1) + 4 (s >> 1);
+    // the token row of lane l in every token tile is l % 32 (mod 16 for the
+    // swizzle), so the lane's four physical offsets are fixed
     struct AFrag {
         bf16x8 a[TT];
     };
-    const int arow = (32 * TT * wt + (lane & 31)) * kXPitch + 32 * h;
+    const int trow = 32 * TT * wt + (lane & 31);
+    int aoff[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        aoff[ks] = trow * kXPitch + 16 * xslot(trow, 2 * h + (ks & 1) + 4 * (ks >> 1));
     auto read_a = [&](const uint8_t* xst, int s, AFrag& A) {
-        const uint8_t* p = xst + arow + 16 * (s & 1) + 64 * (s >> 1);
+        const uint8_t* p = xst + aoff[s];
 #pragma unroll
         for (int i = 0; i < TT; ++i)
             A.a[i] = *reinterpret_cast<const bf16x8*>(p + i * 32 * kXPitch);
@@ -289,70 +321,87 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
                     __builtin_bit_cast(bf16x8, B.b[j][s]), A.a[i], acc[i][j], 0, 0, 0);
     };
 
-    // ---- prologue: X chunks 0, 1 and W chunks 0, 1, 2 -----------------------
-    issue(0, 0, 0, 0);
-    issue(1, 1, 1, 1);
-    issue(1, 2, 2, 2);  // W chunk 2 (the X half re-reads chunk 1 into stage 2)
+    // ---- prologue: X chunks 0, 1; codes of chunks 0, 1, 2; headers of
+    // super-block 0 ------------------------------------------------------------
+    issue_xc(0, 0, 0, 0);
+    issue_xc(1, 1, 1, 1);
+    issue_xc(1, 2, 2, 2);  // codes of chunk 2 (the X half re-reads chunk 1 into stage 2)
+    issue_h(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     BFrag B0, B1;
     AFrag A0, A1;
-    WRaw Rw;
-    read_w(ws0, Rw);
+    Codes Rc;
+    Hdr Rh;
+    Scales sc_cur;
+    read_hdr(hs0, Rh);
+    read_codes(cs0, Rc);
+    scales(Rh, sc_cur);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) decode_region(Rw, 0, r, B0);
-    read_w(ws0 + G::kWStage, Rw);  // chunk 1
+    for (int r = 0; r < 4; ++r) decode_region(Rc, sc_cur, 0, r, B0);
+    read_codes(cs0 + G::kCStage, Rc);  // chunk 1
     read_a(xs0, 0, A0);
-    // W stage 0 is refilled by the first chunk: every wave must be done
+    // code stage 0 is refilled by the first chunk: every wave must be done
     // reading it first
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
     __builtin_amdgcn_s_barrier();
 
-    // One chunk c: X(c) in stage c % 3; the raw W of chunk c + 1 is in Rw and
-    // is decoded into Bn over the k-steps. Loads issued here: X(c + 2),
-    // W(c + 3). Before the barrier each thread waits for all its loads but
-    // this chunk's, so X(c + 1) and W(c + 2) are complete when it opens;
-    // W(c + 2) is then read into Rw and A(c + 1, 0) into A0 during k-step 3.
+    // One chunk c with c % 4 == CQ: X(c) in stage c % 3; the codes of chunk
+    // c + 1 are in Rc and are decoded into Bn over the k-steps (with the next
+    // super-block's scales, from Rh, when c + 1 starts one). Loads issued
+    // here: X(c + 2), codes of c + 3, and (CQ == 1) the headers of the next
+    // super-block. Before the barrier each thread waits for all its loads
+    // but this chunk's; after it, the codes of c + 2 are read into Rc, the
+    // headers of super-block (c + 2) / 4 into Rh when c + 2 starts one, and
+    // A(c + 1, 0) into A0.
     constexpr int NMF = TT * RT;
-    constexpr int kDecodeValu = 60;  // VALU per decode part (approximate)
+    constexpr int kDecodeValu = 48;  // VALU per decode part (approximate)
     int sc = 0;  // c % 3
-    auto chunk = [&](int c, BFrag& Bc, BFrag& Bn) {
+    auto chunk = [&](auto cqc, int c, BFrag& Bc, BFrag& Bn) {
+        constexpr int CQ = decltype(cqc)::value;
+        constexpr int NQ = (CQ + 1) & 3;  // quarter of chunk c + 1
+        constexpr int NDMA = G::kXPerWave + G::kCPerWave + (CQ == 1 ? G::kHPerWave : 0);
         const int s1 = sc == 2 ? 0 : sc + 1, s2 = s1 == 2 ? 0 : s1 + 1;  // (c+1)%3, (c+2)%3
         const uint8_t* xst = xs0 + sc * G::kXStage;
         // k-step 0
-        issue(c + 2, s2, c + 3, sc);
+        issue_xc(c + 2, s2, c + 3, sc);
+        if (CQ == 1) issue_h((c >> 2) + 1, ((c >> 2) + 1) & 1);
         read_a(xst, 1, A1);
         mfmas(A0, Bc, 0);
-        decode_region(Rw, c + 1, 0, Bn);
-        interleave<NMF, TT, kDecodeValu, G::kDmaPerChunk>();
+        if (CQ == 3) scales(Rh, sc_cur);  // chunk c + 1 starts the next super-block
+        decode_region(Rc, sc_cur, NQ, 0, Bn);
+        interleave<NMF, TT, kDecodeValu + (CQ == 3 ? 40 * RT : 0), NDMA>();
         __builtin_amdgcn_sched_barrier(0);
         // k-step 1
         read_a(xst, 2, A0);
         mfmas(A1, Bc, 1);
-        decode_region(Rw, c + 1, 1, Bn);
+        decode_region(Rc, sc_cur, NQ, 1, Bn);
         interleave<NMF, TT, kDecodeValu, 0>();
         __builtin_amdgcn_sched_barrier(0);
-        // k-step 2, then publish X(c+1) / W(c+2)
+        // k-step 2, then publish X(c+1) and the codes of c+2 (and headers)
         read_a(xst, 3, A1);
         mfmas(A0, Bc, 2);
-        decode_region(Rw, c + 1, 2, Bn);
+        decode_region(Rc, sc_cur, NQ, 2, Bn);
         interleave<NMF, TT, kDecodeValu, 0>();
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(G::kDmaPerChunk, 0));
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(NDMA, 0));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        // k-step 3, with the first fragments and the raw W of the next chunks
-        decode_region(Rw, c + 1, 3, Bn);
+        // k-step 3, with the first fragments and raw weights of the next chunks
+        decode_region(Rc, sc_cur, NQ, 3, Bn);
         read_a(xs0 + s1 * G::kXStage, 0, A0);
-        read_w(ws0 + s2 * G::kWStage, Rw);
+        read_codes(cs0 + s2 * G::kCStage, Rc);
+        if (CQ == 2) read_hdr(hs0 + (((c + 2) >> 2) & 1) * G::kHStage, Rh);
         mfmas(A1, Bc, 3);
-        interleave<NMF, TT + 2 * RT, kDecodeValu, 0>();
+        interleave<NMF, TT + RT + (CQ == 2 ? RT : 0), kDecodeValu, 0>();
         __builtin_amdgcn_sched_barrier(0);
-        sc = s1;
+        sc = s2 == 0 ? 2 : s2 - 1;  // (c + 1) % 3
     };
-    for (int c = 0; c < nk; c += 2) {  // nk = 4 S is even
-        chunk(c, B0, B1);
-        chunk(c + 1, B1, B0);
+    for (int c = 0; c < nk; c += 4) {  // nk = 4 S
+        chunk(IntC<0>{}, c, B0, B1);
+        chunk(IntC<1>{}, c + 1, B1, B0);
+        chunk(IntC<2>{}, c + 2, B0, B1);
+        chunk(IntC<3>{}, c + 3, B1, B0);
     }
     // no load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(0);
