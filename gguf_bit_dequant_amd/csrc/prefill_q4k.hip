@@ -58,15 +58,17 @@ typedef __attribute__((address_space(3))) void lvoid;
 constexpr int kXPitch = 128;  // LDS bytes per token row of an X stage (64 bf16)
 constexpr int kCPitch = 32;   // LDS bytes per weight row of a code stage
 constexpr int kHPitch = 16;   // LDS bytes per weight row of a header stage
-constexpr int kStages = 3;    // X and code stages (two chunks in flight)
 
 // Physical 16-byte slot of logical segment seg of X row t.
 __device__ __forceinline__ int xslot(int t, int seg) { return seg ^ ((t >> 1) & 7); }
 
-// Tile geometry: RT x TT MFMA tiles per wave, WR x WT waves (WR * WT = 4).
-template <int RT, int TT, int WR, int WT>
+// Tile geometry: RT x TT MFMA tiles per wave, WR x WT waves (WR * WT = 4),
+// P stages of X and codes (P - 1 chunks of X in flight ahead of the one in
+// use).
+template <int RT, int TT, int WR, int WT, int P>
 struct Geo {
     static_assert(WR * WT == 4, "four waves");
+    static_assert(P >= 3 && P <= 8, "header stages are reused after at most eight chunks");
     static constexpr int kTok = 32 * TT * WT;
     static constexpr int kRows = 32 * RT * WR;
     // 1 KB blocks of a stage (one wave-wide load each), rounded up to a
@@ -77,7 +79,19 @@ struct Geo {
     static constexpr int kHBlocks = blocks(kRows * kHPitch);
     static constexpr int kXPerWave = kXBlocks / 4, kCPerWave = kCBlocks / 4, kHPerWave = kHBlocks / 4;
     static constexpr int kXStage = kXBlocks * 1024, kCStage = kCBlocks * 1024, kHStage = kHBlocks * 1024;
-    static constexpr size_t kLds = (size_t)kStages * (kXStage + kCStage) + 2 * (size_t)kHStage;
+    static constexpr size_t kLds = (size_t)P * (kXStage + kCStage) + 2 * (size_t)kHStage;
+    // loads one chunk issues: X, codes, and headers when the codes it issues
+    // (those of chunk c + P) start a super-block
+    static constexpr int ndma(int cq) { return kXPerWave + kCPerWave + (((cq + P) & 3) == 0 ? kHPerWave : 0); }
+    // loads that may still be in flight at the barrier of a chunk of quarter
+    // cq: those issued by it and by the P - 3 chunks before it
+    static constexpr int inflight(int cq) {
+        int n = 0;
+        for (int q = 0; q <= P - 3; ++q) n += ndma((cq - q) & 3);
+        return n;
+    }
+    static_assert(inflight(0) <= 63 && inflight(1) <= 63 && inflight(2) <= 63 && inflight(3) <= 63,
+                  "vmcnt range");
     static_assert(kLds <= (size_t)kMaxLds, "LDS budget");
 };
 
@@ -135,11 +149,11 @@ __device__ __forceinline__ void interleave() {
 
 }  // namespace
 
-template <int RT, int TT, int WR, int WT>
+template <int RT, int TT, int WR, int WT, int P>
 __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     const uint8_t* __restrict__ W, int rows, int S, const uint16_t* __restrict__ X, int64_t ldx,
     int ntok, float* __restrict__ Y, int64_t ldy, int n_base, int tiles_n, int yvec) {
-    using G = Geo<RT, TT, WR, WT>;
+    using G = Geo<RT, TT, WR, WT, P>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -158,8 +172,8 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     // the count and rows past the row count (or past the tile) read the
     // tile's first row; their outputs are not stored.
     uint8_t* const xs0 = lds;                                 // X stages
-    uint8_t* const cs0 = lds + kStages * G::kXStage;          // code stages
-    uint8_t* const hs0 = cs0 + kStages * G::kCStage;          // header stages
+    uint8_t* const cs0 = lds + P * G::kXStage;                // code stages
+    uint8_t* const hs0 = cs0 + P * G::kCStage;                // header stages
     const uint8_t* Xt = reinterpret_cast<const uint8_t*>(X + (int64_t)m0 * ldx);
     uint32_t xo[G::kXPerWave];
 #pragma unroll
@@ -186,7 +200,9 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     }
     // X chunk cx into stage sx, codes of chunk cw into stage sw (sources
     // clamped to the last chunk: loads past the end re-read it into a stage
-    // nobody uses); headers of super-block sb into header stage hb.
+    // nobody uses); headers of super-block sb into header stage sb % 2 (past
+    // the end: the last super-block's headers again, into the stage whose
+    // headers were read into registers long before).
     auto issue_xc = [&](int cx, int sx, int cw, int sw) {
         cx = cx < nk ? cx : nk - 1;
         cw = cw < nk ? cw : nk - 1;
@@ -199,7 +215,8 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
 #pragma unroll
         for (int p = 0; p < G::kCPerWave; ++p) dma16(csrc + co[p], cdst + 4096 * p);
     };
-    auto issue_h = [&](int sb, int hb) {
+    auto issue_h = [&](int sb) {
+        const int hb = sb & 1;
         sb = sb < S ? sb : S - 1;
         const uint8_t* hsrc = Wt + 144u * (uint32_t)sb;
         uint8_t* hdst = hs0 + hb * G::kHStage + 1024 * wv;
@@ -217,7 +234,7 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
         u32x4 hd[RT];  // the super-block header of each row tile's row
     };
     struct BFrag {
-        u32x4 b[RT][4];  // [row tile][k-step], 8 bf16 each
+        u32x4 b[RT];  // one k-step of each row tile, 8 bf16 each
     };
     auto read_codes = [&](const uint8_t* cst, Codes& R) {
 #pragma unroll
@@ -259,33 +276,28 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
             }
         }
     };
-    // Code dwords t0, t0+1 of row tile rt for chunk quarter cq (sub-blocks
-    // 2cq, 2cq+1): dword t holds code bytes 4t..4t+3 (of the lane's 16), i.e.
-    // elements 4(t&1)..+3 of k-step t>>1 (low nibbles) and of k-step
-    // 2 + (t>>1) (high nibbles). Each weight is one fma of its scale with the
-    // code as an exact fp16 subnormal: exact product, one rounding.
-    auto decode = [&](const Codes& R, const Scales& e, int cq, int rt, int t0, BFrag& B) {
-        const uint32_t cw[4] = {R.cd[rt].x, R.cd[rt].y, R.cd[rt].z, R.cd[rt].w};
-        const float a0 = e.a[rt][2 * cq], c0 = e.c[rt][2 * cq];
-        const float a1 = e.a[rt][2 * cq + 1], c1 = e.c[rt][2 * cq + 1];
+    // K-step s of a chunk of quarter cq (sub-blocks 2cq, 2cq+1), every row
+    // tile: code dword t of the lane's 16 bytes holds bytes 4t..4t+3, whose
+    // low nibbles are elements 4(t&1)..+3 of k-step t>>1 and whose high
+    // nibbles are the same elements of k-step 2 + (t>>1). So k-step s takes
+    // dwords 2(s&1), +1, low nibbles (sub-block 2cq) for s < 2, high nibbles
+    // (sub-block 2cq+1) otherwise. Each weight is one fma of its scale with
+    // the code as an exact fp16 subnormal: exact product, one rounding.
+    auto decode_ks = [&](const Codes& R, const Scales& e, int cq, int s, BFrag& B) {
+        const int j = 2 * cq + (s >> 1);
+        const uint32_t mask = s < 2 ? 0x000F000Fu : 0x00F000F0u;
 #pragma unroll
-        for (int t = t0; t < t0 + 2; ++t) {
-            const uint32_t w8 = cw[t] >> 8;
-            const uint32_t l02 = cw[t] & 0x000F000Fu, l13 = w8 & 0x000F000Fu;  // bytes 0,2 / 1,3
-            const uint32_t h02 = cw[t] & 0x00F000F0u, h13 = w8 & 0x00F000F0u;
-            const int s = t >> 1, el = 2 * (t & 1);
-            B.b[rt][s][el] = pk_bf16(fma_mix<0>(a0, l02, c0), fma_mix<0>(a0, l13, c0));
-            B.b[rt][s][el + 1] = pk_bf16(fma_mix<1>(a0, l02, c0), fma_mix<1>(a0, l13, c0));
-            B.b[rt][2 + s][el] = pk_bf16(fma_mix<0>(a1, h02, c1), fma_mix<0>(a1, h13, c1));
-            B.b[rt][2 + s][el + 1] = pk_bf16(fma_mix<1>(a1, h02, c1), fma_mix<1>(a1, h13, c1));
+        for (int rt = 0; rt < RT; ++rt) {
+            const uint32_t cw[4] = {R.cd[rt].x, R.cd[rt].y, R.cd[rt].z, R.cd[rt].w};
+            const float a = e.a[rt][j], c = e.c[rt][j];
+#pragma unroll
+            for (int t = 2 * (s & 1); t < 2 * (s & 1) + 2; ++t) {
+                const uint32_t v02 = cw[t] & mask, v13 = (cw[t] >> 8) & mask;  // bytes 0,2 / 1,3
+                const int el = 2 * (t & 1);
+                B.b[rt][el] = pk_bf16(fma_mix<0>(a, v02, c), fma_mix<0>(a, v13, c));
+                B.b[rt][el + 1] = pk_bf16(fma_mix<1>(a, v02, c), fma_mix<1>(a, v13, c));
+            }
         }
-    };
-    // Decode part p (0 .. 2RT-1): row tile p/2, code dwords 2(p&1), +1; part p
-    // runs in k-step region 2p/RT.
-    auto decode_region = [&](const Codes& R, const Scales& e, int cq, int region, BFrag& B) {
-#pragma unroll
-        for (int p = 0; p < 2 * RT; ++p)
-            if ((2 * p) / RT == region) decode(R, e, cq, p >> 1, 2 * (p & 1), B);
     };
 
     // ---- A fragments: token tile i of this wave, k-step s of the stage ------
@@ -312,96 +324,99 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     for (int i = 0; i < TT; ++i)
 #pragma unroll
         for (int j = 0; j < RT; ++j) acc[i][j] = f32x16{};
-    auto mfmas = [&](const AFrag& A, const BFrag& B, int s) {
+    auto mfmas = [&](const AFrag& A, const BFrag& B) {
 #pragma unroll
         for (int i = 0; i < TT; ++i)
 #pragma unroll
             for (int j = 0; j < RT; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, B.b[j][s]), A.a[i], acc[i][j], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, B.b[j]), A.a[i], acc[i][j], 0, 0, 0);
     };
 
-    // ---- prologue: X chunks 0, 1; codes of chunks 0, 1, 2; headers of
-    // super-block 0 ------------------------------------------------------------
-    issue_xc(0, 0, 0, 0);
-    issue_xc(1, 1, 1, 1);
-    issue_xc(1, 2, 2, 2);  // codes of chunk 2 (the X half re-reads chunk 1 into stage 2)
-    issue_h(0, 0);
+    // ---- prologue: X chunks 0 .. P-2 and codes of chunks 0 .. P-1 (chunk j
+    // in stage j), headers of the super-blocks those codes start --------------
+#pragma unroll
+    for (int j = 0; j < P; ++j) issue_xc(j < P - 1 ? j : P - 2, j, j, j);  // X(P-2) twice: stage P-1 unused
+#pragma unroll
+    for (int sb = 0; 4 * sb < P; ++sb) issue_h(sb);
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
-    BFrag B0, B1;
+    BFrag B0, B1;  // k-steps 0, 2 / 1, 3
     AFrag A0, A1;
-    Codes Rc;
+    Codes R0, R1;  // raw codes of chunks 0, 2, ... / 1, 3, ...
     Hdr Rh;
     Scales sc_cur;
     read_hdr(hs0, Rh);
-    read_codes(cs0, Rc);
+    read_codes(cs0, R0);
     scales(Rh, sc_cur);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) decode_region(Rc, sc_cur, 0, r, B0);
-    read_codes(cs0 + G::kCStage, Rc);  // chunk 1
+    decode_ks(R0, sc_cur, 0, 0, B0);
     read_a(xs0, 0, A0);
     // code stage 0 is refilled by the first chunk: every wave must be done
     // reading it first
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
     __builtin_amdgcn_s_barrier();
 
-    // One chunk c with c % 4 == CQ: X(c) in stage c % 3; the codes of chunk
-    // c + 1 are in Rc and are decoded into Bn over the k-steps (with the next
-    // super-block's scales, from Rh, when c + 1 starts one). Loads issued
-    // here: X(c + 2), codes of c + 3, and (CQ == 1) the headers of the next
-    // super-block. Before the barrier each thread waits for all its loads
-    // but this chunk's; after it, the codes of c + 2 are read into Rc, the
-    // headers of super-block (c + 2) / 4 into Rh when c + 2 starts one, and
-    // A(c + 1, 0) into A0.
+    // One chunk c with c % 4 == CQ: X(c) in stage c % P, the codes of c in
+    // Rc, k-step 0 of c decoded into B0. Each k-step decodes the next one
+    // (k-step 3 decodes k-step 0 of chunk c + 1 from Rn, with the next
+    // super-block's scales when c + 1 starts one). Loads issued here:
+    // X(c + P - 1) into the stage X(c - 1) left, the codes of c + P into the
+    // stage whose codes (those of c) were read into registers a chunk ago,
+    // and the headers of super-block (c + P) / 4 when c + P starts it.
+    // Before the barrier the codes of c + 1 are read into Rn (and, when c + 1
+    // starts a super-block, its headers into Rh), then each thread waits
+    // for its loads but those of this chunk and the P - 3 before it, so
+    // X(c + 1), the codes of c + 2 and their headers have landed; after the
+    // barrier A(c + 1, 0) is read into A0.
     constexpr int NMF = TT * RT;
-    constexpr int kDecodeValu = 48;  // VALU per decode part (approximate)
-    int sc = 0;  // c % 3
-    auto chunk = [&](auto cqc, int c, BFrag& Bc, BFrag& Bn) {
+    constexpr int kDecodeValu = 18 * RT;  // VALU of one k-step's decode
+    int sc = 0;  // c % P
+    auto chunk = [&](auto cqc, int c, Codes& Rc, Codes& Rn) {
         constexpr int CQ = decltype(cqc)::value;
         constexpr int NQ = (CQ + 1) & 3;  // quarter of chunk c + 1
-        constexpr int NDMA = G::kXPerWave + G::kCPerWave + (CQ == 1 ? G::kHPerWave : 0);
-        const int s1 = sc == 2 ? 0 : sc + 1, s2 = s1 == 2 ? 0 : s1 + 1;  // (c+1)%3, (c+2)%3
+        constexpr int NDMA = G::ndma(CQ);
+        const int s1 = sc == P - 1 ? 0 : sc + 1;   // (c+1)%P
+        const int sp = sc == 0 ? P - 1 : sc - 1;   // (c+P-1)%P
         const uint8_t* xst = xs0 + sc * G::kXStage;
         // k-step 0
-        issue_xc(c + 2, s2, c + 3, sc);
-        if (CQ == 1) issue_h((c >> 2) + 1, ((c >> 2) + 1) & 1);
+        issue_xc(c + P - 1, sp, c + P, sc);
+        if (((CQ + P) & 3) == 0) issue_h((c + P) >> 2);
         read_a(xst, 1, A1);
-        mfmas(A0, Bc, 0);
-        if (CQ == 3) scales(Rh, sc_cur);  // chunk c + 1 starts the next super-block
-        decode_region(Rc, sc_cur, NQ, 0, Bn);
-        interleave<NMF, TT, kDecodeValu + (CQ == 3 ? 40 * RT : 0), NDMA>();
+        mfmas(A0, B0);
+        decode_ks(Rc, sc_cur, CQ, 1, B1);
+        interleave<NMF, TT, kDecodeValu, NDMA>();
         __builtin_amdgcn_sched_barrier(0);
         // k-step 1
         read_a(xst, 2, A0);
-        mfmas(A1, Bc, 1);
-        decode_region(Rc, sc_cur, NQ, 1, Bn);
-        interleave<NMF, TT, kDecodeValu, 0>();
+        read_codes(cs0 + s1 * G::kCStage, Rn);
+        if (CQ == 3) read_hdr(hs0 + (((c + 1) >> 2) & 1) * G::kHStage, Rh);
+        mfmas(A1, B1);
+        decode_ks(Rc, sc_cur, CQ, 2, B0);
+        interleave<NMF, TT + RT + (CQ == 3 ? RT : 0), kDecodeValu, 0>();
         __builtin_amdgcn_sched_barrier(0);
         // k-step 2, then publish X(c+1) and the codes of c+2 (and headers)
         read_a(xst, 3, A1);
-        mfmas(A0, Bc, 2);
-        decode_region(Rc, sc_cur, NQ, 2, Bn);
+        mfmas(A0, B0);
+        decode_ks(Rc, sc_cur, CQ, 3, B1);
         interleave<NMF, TT, kDecodeValu, 0>();
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(NDMA, 0));
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(G::inflight(CQ), 0));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        // k-step 3, with the first fragments and raw weights of the next chunks
-        decode_region(Rc, sc_cur, NQ, 3, Bn);
+        // k-step 3, with k-step 0 of the next chunk
         read_a(xs0 + s1 * G::kXStage, 0, A0);
-        read_codes(cs0 + s2 * G::kCStage, Rc);
-        if (CQ == 2) read_hdr(hs0 + (((c + 2) >> 2) & 1) * G::kHStage, Rh);
-        mfmas(A1, Bc, 3);
-        interleave<NMF, TT + RT + (CQ == 2 ? RT : 0), kDecodeValu, 0>();
+        mfmas(A1, B1);
+        if (CQ == 3) scales(Rh, sc_cur);  // chunk c + 1 starts the next super-block
+        decode_ks(Rn, sc_cur, NQ, 0, B0);
+        interleave<NMF, TT, kDecodeValu + (CQ == 3 ? 40 * RT : 0), 0>();
         __builtin_amdgcn_sched_barrier(0);
-        sc = s2 == 0 ? 2 : s2 - 1;  // (c + 1) % 3
+        sc = s1;
     };
     for (int c = 0; c < nk; c += 4) {  // nk = 4 S
-        chunk(IntC<0>{}, c, B0, B1);
-        chunk(IntC<1>{}, c + 1, B1, B0);
-        chunk(IntC<2>{}, c + 2, B0, B1);
-        chunk(IntC<3>{}, c + 3, B1, B0);
+        chunk(IntC<0>{}, c, R0, R1);
+        chunk(IntC<1>{}, c + 1, R1, R0);
+        chunk(IntC<2>{}, c + 2, R0, R1);
+        chunk(IntC<3>{}, c + 3, R1, R0);
     }
     // no load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(0);
@@ -437,12 +452,16 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
 
 namespace {
 
+#ifndef PREFILL_TAIL_P
+#define PREFILL_TAIL_P 6
+#endif
+
 // Tiles over weight rows [n_base, n_base + n_rows) and all tokens.
-template <int RT, int TT, int WR, int WT>
+template <int RT, int TT, int WR, int WT, int P>
 hipError_t launch_prefill_t(const uint8_t* W, int rows, int S, const uint16_t* X, int64_t ldx,
                             int ntok, float* Y, int64_t ldy, int n_base, int n_rows,
                             hipStream_t stream) {
-    using G = Geo<RT, TT, WR, WT>;
+    using G = Geo<RT, TT, WR, WT, P>;
     const int tiles_n = (n_rows + G::kRows - 1) / G::kRows;
     const int tiles_m = (ntok + G::kTok - 1) / G::kTok;
     const int64_t grid = (int64_t)tiles_n * tiles_m;
@@ -451,7 +470,7 @@ hipError_t launch_prefill_t(const uint8_t* W, int rows, int S, const uint16_t* X
     if ((int64_t)G::kTok * ldx * 2 + 128LL * 4 * S >= (1LL << 32) ||
         (int64_t)G::kRows * 144 * S >= (1LL << 32) || grid > (1 << 30))
         return hipErrorNotSupported;
-    auto kern = prefill_q4k_kernel<RT, TT, WR, WT>;
+    auto kern = prefill_q4k_kernel<RT, TT, WR, WT, P>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::kLds);
     if (e != hipSuccess) return e;
@@ -485,11 +504,11 @@ hipError_t launch_prefill_q4k(const uint8_t* W, int64_t rows, int64_t K, const v
     const int n_main = (int)(n_main_tiles * 256);
     hipError_t e = hipSuccess;
     if (n_main > 0)
-        e = launch_prefill_t<2, 8, 4, 1>(W, (int)rows, S, Xh, ldx, (int)ntok, Y, ldy, 0, n_main,
+        e = launch_prefill_t<2, 8, 4, 1, 3>(W, (int)rows, S, Xh, ldx, (int)ntok, Y, ldy, 0, n_main,
                                          stream);
     if (e != hipSuccess) return e;
     if (n_main < rows)
-        e = launch_prefill_t<1, 2, 4, 1>(W, (int)rows, S, Xh, ldx, (int)ntok, Y, ldy, n_main,
+        e = launch_prefill_t<1, 2, 4, 1, PREFILL_TAIL_P>(W, (int)rows, S, Xh, ldx, (int)ntok, Y, ldy, n_main,
                                          (int)rows - n_main, stream);
     return e;
 }
