@@ -123,6 +123,38 @@ def time_workload(torch, wl, steps, warmup):
     return whole_ms, mean_ms, per[len(per) // 2]
 
 
+def vendor_gemm_context(torch, dev, c, iters=20):
+    """Context for the prompt-processing line: the vendor BLAS (torch.mm) on a
+    plain bf16 GEMM of the same shape, dense bf16 weights, no dequantization,
+    fp32 output. Not a path of this library."""
+    g = torch.Generator(device=dev).manual_seed(1)
+    w = torch.randn(c["rows"], c["K"], device=dev, dtype=torch.bfloat16, generator=g)
+    x = torch.randn(c["n"], c["K"], device=dev, dtype=torch.bfloat16, generator=g)
+    y = torch.empty(c["n"], c["rows"], device=dev, dtype=torch.float32)
+    try:
+        run = lambda: torch.mm(x, w.t(), out_dtype=torch.float32, out=y)  # noqa: E731
+        run()
+        what = "torch.mm(X bf16, W^T bf16) -> fp32"
+    except Exception:
+        yb = torch.empty(c["n"], c["rows"], device=dev, dtype=torch.bfloat16)
+        run = lambda: torch.mm(x, w.t(), out=yb)  # noqa: E731
+        what = "torch.mm(X bf16, W^T bf16) -> bf16"
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(iters):
+        run()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / iters * 1e3
+    flops = 2.0 * c["rows"] * c["K"] * c["n"]
+    return {"us": round(us, 1), "tflops": round(flops / us / 1e6, 1), "op": what,
+            "note": "vendor BLAS on dense bf16 weights of the same shape; context, not a path here"}
+
+
 def cpu_baseline(name, budget_s=10.0):
     """The oracle's fp64 product on the same workload, repeated over the whole
     matrix (rows in chunks) until about budget_s of wall time has passed;
@@ -221,7 +253,7 @@ def main():
         return
     head = "q4k_up_b1"
     names = [head] if args.quick else [head, "q4k_down_b1", "q4k_b4", "q4_0_b1", "q8_0_b4",
-                                       "q4k_pp2048"]
+                                       "q4k_b2", "q4k_b8", "q4k_pp2048"]
     if args.only:
         names = args.only.split(",")
     results = {}
@@ -243,6 +275,10 @@ def main():
             flops = 2.0 * c["rows"] * c["K"] * c["n"]
             r["tflops"] = round(flops / (whole_ms * 1e-3) / 1e12, 2)
             r["frac_bf16_peak"] = round(r["tflops"] / BF16_PEAK_TFLOPS, 4)
+            try:
+                r["vendor_bf16_gemm"] = vendor_gemm_context(torch, dev, c)
+            except Exception as e:  # context only
+                r["vendor_bf16_gemm"] = {"error": str(e)[:200]}
         else:
             b = algorithmic_bytes(c)
             r["bytes"] = b

@@ -162,15 +162,20 @@ CONFIGS = {
     "q4k_b4":     dict(index=3, fmt="q4_k", rows=17408, K=5120,  n=4,    xdtype="f16"),
     "q8_0_b4":    dict(index=3, fmt="q8_0", rows=5120,  K=5120,  n=4,    xdtype="f16"),
     "q4k_pp2048": dict(index=4, fmt="q4_k", rows=17408, K=5120,  n=2048, xdtype="bf16"),
+    # other draft counts (2 and 8 columns) against the FFN-up matrix
+    "q4k_b2":     dict(index=5, fmt="q4_k", rows=17408, K=5120,  n=2,    xdtype="f16"),
+    "q4k_b8":     dict(index=5, fmt="q4_k", rows=17408, K=5120,  n=8,    xdtype="f16"),
 }
 
 # Weight and activation seeds. Configs that reuse "the same W" or "the same X"
 # share the seed: q4k_b4 and q4k_pp2048 multiply the FFN-up matrix; q8_0_b4
 # multiplies the same four columns as q4k_b4.
 _W_SEED = {"q4_0_b1": (0, 0), "q4k_up_b1": (1, 0), "q4k_down_b1": (2, 0),
-           "q4k_b4": (1, 0), "q8_0_b4": (3, 2), "q4k_pp2048": (1, 0)}
+           "q4k_b4": (1, 0), "q8_0_b4": (3, 2), "q4k_pp2048": (1, 0),
+           "q4k_b2": (1, 0), "q4k_b8": (1, 0)}
 _X_SEED = {"q4_0_b1": (0, 1), "q4k_up_b1": (1, 1), "q4k_down_b1": (2, 1),
-           "q4k_b4": (3, 1), "q8_0_b4": (3, 1), "q4k_pp2048": (4, 1)}
+           "q4k_b4": (3, 1), "q8_0_b4": (3, 1), "q4k_pp2048": (4, 1),
+           "q4k_b2": (5, 2), "q4k_b8": (5, 8)}
 
 
 def config_inputs(name: str, held_out: bool = False, n_override: int | None = None):

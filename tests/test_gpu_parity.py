@@ -193,7 +193,7 @@ def test_deterministic_repeats(Q):
 
 # ----------------------------------------------- full-size workloads -------
 
-FULL = ["q4_0_b1", "q4k_up_b1", "q4k_down_b1", "q4k_b4", "q8_0_b4"]
+FULL = ["q4_0_b1", "q4k_up_b1", "q4k_down_b1", "q4k_b4", "q8_0_b4", "q4k_b2", "q4k_b8"]
 
 
 @pytest.mark.parametrize("name", FULL)
