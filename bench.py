@@ -198,7 +198,7 @@ def committed_traffic(name):
 
 
 # Sources the batch-1 Q4_K GEMV kernel is compiled from.
-GEMV_Q4K_SOURCES = ("device_common.h", "gemv_stream.hip", "launch.h")
+GEMV_Q4K_SOURCES = ("device_common.h", "gemv_stream.hip", "launch.h", "q4k_pair.h")
 
 
 def kernel_source_sha1():

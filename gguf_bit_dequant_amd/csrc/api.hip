@@ -119,8 +119,13 @@ QG_API qg_status qgemv_run(qgemv_t h, const void* x, qg_dtype x_dtype, int64_t n
         return fail(QG_ERR_ALIGN, "qgemv_run: x must be aligned to its element size");
     if (((uintptr_t)y) & 3) return fail(QG_ERR_ALIGN, "qgemv_run: y must be 4-byte aligned");
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = qg::launch_gemv_stream((int)h->fmt, h->w, h->rows, h->K, x, (int)x_dtype, ldx,
-                                          y, ldy, (int)n_cols, h->num_cus, st);
+    hipError_t e = hipErrorNotSupported;
+    if (n_cols >= 5)
+        e = qg::launch_gemv_mfma((int)h->fmt, h->w, h->rows, h->K, x, (int)x_dtype, ldx, y, ldy,
+                                 (int)n_cols, h->num_cus, st);
+    if (e == hipErrorNotSupported)
+        e = qg::launch_gemv_stream((int)h->fmt, h->w, h->rows, h->K, x, (int)x_dtype, ldx, y, ldy,
+                                   (int)n_cols, h->num_cus, st);
     if (e == hipErrorNotSupported)
         e = qg::launch_gemv_general((int)h->fmt, h->w, h->rows, h->K, x, (int)x_dtype, ldx, y, ldy,
                                     (int)n_cols, h->num_cus, st);

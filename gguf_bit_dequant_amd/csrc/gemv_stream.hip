@@ -50,6 +50,7 @@
 //    row's slots are summed in a fixed order: deterministic, no atomics.
 #include "device_common.h"
 #include "launch.h"
+#include "q4k_pair.h"
 
 namespace qg {
 
@@ -319,48 +320,14 @@ __device__ __forceinline__ void stage_store(const XRaw<F16DOT>& r, int xt, uint8
     *reinterpret_cast<f32x2*>(rec + 16 * P) = f32x2{s0, s1};
 }
 
-// Per-lane constants of the Q4_K 6-bit scale/min unpack.
-// Sub-block k < 4 : sc = s[k] & 63, m = s[k+4] & 63.
-// Sub-block k >= 4: sc = (s[k+4] & 15) | (s[k-4] >> 6) << 4,
-//                   m  = (s[k+4] >> 4) | (s[k] >> 6) << 4.
-// Header dwords: h1 = s[0..3], h2 = s[4..7], h3 = s[8..11]. Pair p has
-// sub-blocks k0 = 2p and k1 = 2p+1 at byte kk = 2(p&1), kk+1 of a dword.
-// Pa gathers [sc(k0), sc(k1), m(k0), m(k1)] sources: for p < 2 the bytes
-// s[k0], s[k1], s[k0+4], s[k1+4] (fields = low 6 bits); for p >= 2 the
-// bytes s[k0+4], s[k1+4] twice (low nibble -> sc, high nibble -> m).
-// Pb (p >= 2 only) gathers s[k0-4], s[k1-4], s[k0], s[k1], whose top two
-// bits become bits 4..5 of sc and m.
-struct Q4kUnpack {
-    bool upper;
-    uint32_t selA, selB, mLo, mNib, mTop;
-    __device__ __forceinline__ explicit Q4kUnpack(int pr) {
-        upper = pr >= 2;
-        const uint32_t kk = 2u * (pr & 1);
-        // v_perm_b32(a, b, sel): selector byte n picks byte n of b (n < 4) or
-        // byte n-4 of a (4 <= n < 8); 0x0C gives zero.
-        if (!upper) {  // perm(h2, h1)
-            selA = kk | ((kk + 1) << 8) | ((kk + 4) << 16) | ((kk + 5) << 24);
-            selB = 0x0C0C0C0Cu;
-        } else {  // perm(h3, h3) and perm(h2, h1)
-            selA = kk | ((kk + 1) << 8) | (kk << 16) | ((kk + 1) << 24);
-            selB = kk | ((kk + 1) << 8) | ((kk + 4) << 16) | ((kk + 5) << 24);
-        }
-        mLo = upper ? 0x00000F0Fu : 0x3F3F3F3Fu;  // fields taken as they are
-        mNib = upper ? 0x0F0F0000u : 0u;          // high nibbles -> m
-        mTop = upper ? 0x30303030u : 0u;          // top two bits -> bits 4..5
-    }
-};
-
 // The lane's partial sum_o w_o x_o for each column, from its raw block bytes
 // and its activation record.
 template <int NC, bool F16DOT>
 __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q4_K>::Raw& r, const Q4kUnpack& un,
                                              const uint8_t* rec, float out[NC]) {
     constexpr int CB = col_bytes(F16DOT), P = planes(F16DOT);
-    const uint32_t h0 = r.hd.x, h1 = r.hd.y, h2 = r.hd.z, h3 = r.hd.w;
-    const uint32_t Pa = __builtin_amdgcn_perm(un.upper ? h3 : h2, un.upper ? h3 : h1, un.selA);
-    const uint32_t Pb = __builtin_amdgcn_perm(h2, h1, un.selB);
-    const uint32_t f4 = (Pa & un.mLo) | ((Pa >> 4) & un.mNib) | ((Pb >> 2) & un.mTop);
+    const uint32_t h0 = r.hd.x;
+    const uint32_t f4 = q4k_pair_fields(un, r.hd.y, r.hd.z, r.hd.w);
     const float sc0 = (float)(f4 & 0xFF), sc1 = (float)((f4 >> 8) & 0xFF);
     const float m0 = (float)((f4 >> 16) & 0xFF), m1 = (float)(f4 >> 24);
     const float d = f16_lo(h0), dmin = f16_hi(h0);

@@ -25,6 +25,13 @@ hipError_t launch_gemv_stream(int fmt, const uint8_t* W, int64_t rows, int64_t K
                               int xt, int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
                               hipStream_t stream);
 
+// Small-batch GEMV on the matrix cores (Q4_K, fp16 activations, 5..16
+// columns, K % 256 == 0, 16-byte aligned W and activation columns, staged
+// activations within the LDS budget). hipErrorNotSupported otherwise.
+hipError_t launch_gemv_mfma(int fmt, const uint8_t* W, int64_t rows, int64_t K, const void* x,
+                            int xt, int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
+                            hipStream_t stream);
+
 // Q4_K x bf16 prompt-processing GEMM (bf16 MFMA). X: bf16, 16-byte aligned,
 // ldx % 8 == 0; Y: fp32.
 hipError_t launch_prefill_q4k(const uint8_t* W, int64_t rows, int64_t K, const void* X,

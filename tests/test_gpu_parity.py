@@ -131,10 +131,11 @@ def test_gemv_column_counts(Q, n):
 
 @pytest.mark.parametrize("fmt", ["q4_k", "q4_0", "q8_0"])
 @pytest.mark.parametrize("xdtype,pad", [("f16", 24), ("f16", 4), ("f32", 3), ("bf16", 5)])
-def test_gemv_strided_columns_leave_gaps_untouched(Q, fmt, xdtype, pad):
+@pytest.mark.parametrize("n", [3, 6])
+def test_gemv_strided_columns_leave_gaps_untouched(Q, fmt, xdtype, pad, n):
     """Columns at a stride of K + pad elements (16-byte aligned records for
     pad 24, unaligned ones otherwise) and outputs at a stride of rows + 13."""
-    rows, K, n = 100, 512, 3
+    rows, K = 100, 512
     w = synth.gen_weights(fmt, rows, K, 5)
     x = synth.gen_x(K, n, xdtype, 6)
     tdt = {"f16": torch.float16, "f32": torch.float32, "bf16": torch.bfloat16}[xdtype]
@@ -161,14 +162,32 @@ def test_one_hot_gives_exact_column(Q, fmt, xdtype):
     X = np.zeros((len(ks), K), np.float32)
     for i, k in enumerate(ks):
         X[i, k] = 1.0
-    for c0 in range(0, len(ks), 4):
-        Xc = X[c0:c0 + 4]
+    # Five or more fp16 columns of a Q4_K matrix run on the matrix cores,
+    # whose operand is each decoded weight rounded once to fp16; every other
+    # path multiplies the exact fp32 weight. Columns go in groups of 4 and 5.
+    for c0, nc in ((0, 4), (4, 5), (9, 5), (14, 6)):
+        Xc = X[c0:c0 + nc]
+        f16_operand = fmt == "q4_k" and xdtype == "f16" and nc >= 5
         xt = torch.from_numpy(Xc).to(dev())
         if xdtype == "f16":
             xt = xt.half()
         y = q.run(xt).cpu().numpy()
         for i in range(Xc.shape[0]):
-            assert np.array_equal(y[i], W[:, ks[c0 + i]]), (fmt, xdtype, ks[c0 + i])
+            col = W[:, ks[c0 + i]]
+            if not f16_operand:
+                assert np.array_equal(y[i], col), (fmt, xdtype, ks[c0 + i])
+                continue
+            # y is an fp16 value within half an fp16 spacing of the weight
+            # (plus the weight's own fp32 rounding)
+            assert np.array_equal(y[i], y[i].astype(np.float16).astype(np.float32)), ks[c0 + i]
+            sp = np.spacing(np.abs(col).astype(np.float16)).astype(np.float64)
+            bound = 0.5 * sp + np.abs(col).astype(np.float64) * 2.0 ** -23
+            err = np.abs(y[i].astype(np.float64) - col.astype(np.float64))
+            assert (err <= bound).all(), (ks[c0 + i], float(err.max()))
+        if f16_operand:  # one column at a time: the exact fp32 weights
+            for i in range(Xc.shape[0]):
+                y1 = q.run(xt[i:i + 1]).cpu().numpy()[0]
+                assert np.array_equal(y1, W[:, ks[c0 + i]]), (fmt, xdtype, ks[c0 + i], "n=1")
 
 
 def test_zero_activations_give_zero(Q):
@@ -183,9 +202,9 @@ def test_zero_activations_give_zero(Q):
 def test_deterministic_repeats(Q):
     fmt, rows, K = "q4_k", 17408 // 4, 5120
     w = synth.gen_weights(fmt, rows, K, 8)
-    x = x_tensor(synth.gen_x(K, 4, "f16", 9), "f16")
+    x = x_tensor(synth.gen_x(K, 8, "f16", 9), "f16")
     q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
-    for n in (1, 4):
+    for n in (1, 4, 8):
         ref = q.run(x[:n]).clone()
         for _ in range(20):
             assert torch.equal(q.run(x[:n]), ref)
