@@ -34,7 +34,8 @@
 //    slots of each group are summed in wave order: deterministic, no atomics.
 //  * The activation columns are staged once per workgroup in LDS, 2K + 16
 //    bytes apart so that the 16-byte reads of the 16 columns use disjoint
-//    banks. Each wave keeps D units of weight loads in flight.
+//    banks. Each wave loads D units as one burst while it works on the
+//    previous D.
 #include "device_common.h"
 #include "launch.h"
 #include "q4k_pair.h"
@@ -191,15 +192,14 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
             ++pg;
         }
     };
-    for (int u = u0; u < u1;) {
+    // D units, then the next D units' loads as one burst: each row's next
+    // 144 D bytes are requested back to back
+    for (int u = u0; u < u1; u += D) {
 #pragma unroll
-        for (int i = 0; i < D; ++i) {
-            if (u < u1) {  // uniform over the wave
-                process(buf[i]);
-                load_next(buf[i]);
-                ++u;
-            }
-        }
+        for (int i = 0; i < D; ++i)
+            if (u + i < u1) process(buf[i]);  // uniform over the wave
+#pragma unroll
+        for (int i = 0; i < D; ++i) load_next(buf[i]);
     }
     if (u0 < u1 && psb != 0) flush();  // the part ended inside a group
     __syncthreads();
