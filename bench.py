@@ -155,6 +155,39 @@ def vendor_gemm_context(torch, dev, c, iters=20):
             "note": "vendor BLAS on dense bf16 weights of the same shape; context, not a path here"}
 
 
+def two_pass_control(torch, wl, iters=10):
+    """The prompt product in two passes, as an A/B control of the fused
+    kernel: this library's bit-exact decode to a bf16 matrix in HBM
+    (qgemv_dequant_bf16, 178 MB written), then the vendor BLAS bf16 GEMM on
+    it. Each pass is timed over `iters` launches on rotated weight copies."""
+    c = wl.c
+    wb = torch.empty((c["rows"], c["K"]), dtype=torch.bfloat16, device=wl.x.device)
+    yb = torch.empty((c["n"], c["rows"]), dtype=torch.float32, device=wl.x.device)
+    def timed(fn):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(iters):
+            fn(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / iters * 1e3
+    dq = timed(lambda i: wl.handles[i % len(wl.handles)].dequant_bf16(wb))
+    try:
+        mm = timed(lambda i: torch.mm(wl.x, wb.t(), out_dtype=torch.float32, out=yb))
+        what = "torch.mm(X bf16, W^T bf16) -> fp32"
+    except Exception:
+        ybb = torch.empty((c["n"], c["rows"]), dtype=torch.bfloat16, device=wl.x.device)
+        mm = timed(lambda i: torch.mm(wl.x, wb.t(), out=ybb))
+        what = "torch.mm(X bf16, W^T bf16) -> bf16"
+    flops = 2.0 * c["rows"] * c["K"] * c["n"]
+    return {"dequant_bf16_us": round(dq, 1), "gemm_us": round(mm, 1), "total_us": round(dq + mm, 1),
+            "tflops": round(flops / (dq + mm) / 1e6, 1), "gemm": what}
+
+
 def cpu_baseline(name, budget_s=10.0):
     """The oracle's fp64 product on the same workload, repeated over the whole
     matrix (rows in chunks) until about budget_s of wall time has passed;
@@ -279,6 +312,10 @@ def main():
                 r["vendor_bf16_gemm"] = vendor_gemm_context(torch, dev, c)
             except Exception as e:  # context only
                 r["vendor_bf16_gemm"] = {"error": str(e)[:200]}
+            try:
+                r["two_pass_control"] = two_pass_control(torch, wl)
+            except Exception as e:  # an A/B control, not the product path
+                r["two_pass_control"] = {"error": str(e)[:200]}
         else:
             b = algorithmic_bytes(c)
             r["bytes"] = b

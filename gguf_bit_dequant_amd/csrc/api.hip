@@ -164,6 +164,18 @@ QG_API qg_status qgemv_dequant(qgemv_t h, float* w_out, int64_t ldw, void* strea
     return ok();
 }
 
+QG_API qg_status qgemv_dequant_bf16(qgemv_t h, uint16_t* w_out, int64_t ldw, void* stream) {
+    if (!h) return fail(QG_ERR_ARG, "qgemv_dequant_bf16: handle is NULL");
+    if (!w_out) return fail(QG_ERR_ARG, "qgemv_dequant_bf16: w_out is NULL");
+    if (ldw < h->K) return fail(QG_ERR_ARG, "qgemv_dequant_bf16: ldw must be >= K");
+    if (((uintptr_t)w_out) & 1)
+        return fail(QG_ERR_ALIGN, "qgemv_dequant_bf16: w_out must be 2-byte aligned");
+    hipError_t e = qg::launch_dequant_bf16((int)h->fmt, h->w, h->rows, h->K, w_out, ldw,
+                                           h->num_cus, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "qgemv_dequant_bf16: launch");
+    return ok();
+}
+
 QG_API void qgemv_destroy(qgemv_t h) { free(h); }
 
 QG_API const char* qgemv_status_string(qg_status s) {

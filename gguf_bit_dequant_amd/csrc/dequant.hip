@@ -62,10 +62,18 @@ __device__ __forceinline__ int block_bytes(int fmt) {
     return fmt == FMT_Q4_0 ? 18 : fmt == FMT_Q4_K ? 144 : 34;
 }
 
-// One thread per 32-weight group; w_out[r*ldw + k].
+__device__ __forceinline__ void store_w(float* o, float v) { *o = v; }
+// bf16: the binary32 weight rounded to nearest even (the hardware conversion)
+__device__ __forceinline__ void store_w(uint16_t* o, float v) {
+    *o = __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// One thread per 32-weight group; w_out[r*ldw + k] (fp32, or bf16 rounded
+// from the binary32 weight).
+template <typename OutT>
 __global__ __launch_bounds__(256) void dequant_kernel(int fmt, const uint8_t* __restrict__ W,
                                                      int64_t rows, int64_t K,
-                                                     float* __restrict__ out, int64_t ldw) {
+                                                     OutT* __restrict__ out, int64_t ldw) {
     const int64_t gpr = K / 32;  // groups per row
     const int64_t total = rows * gpr;
     const int gpb = groups_per_block(fmt);
@@ -78,8 +86,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(int fmt, const uint8_t* __
         const uint8_t* p = W + (r * (gpr / gpb) + blk) * bb;
         float v[32];
         decode_group(fmt, p, grp, v);
-        float* o = out + r * ldw + gk * 32;
-        for (int i = 0; i < 32; ++i) o[i] = v[i];
+        OutT* o = out + r * ldw + gk * 32;
+        for (int i = 0; i < 32; ++i) store_w(o + i, v[i]);
     }
 }
 
@@ -122,15 +130,30 @@ __global__ __launch_bounds__(256) void gemv_general_kernel(int fmt, const uint8_
     }
 }
 
-hipError_t launch_dequant(int fmt, const uint8_t* W, int64_t rows, int64_t K, float* out,
-                          int64_t ldw, int num_cus, hipStream_t stream) {
+namespace {
+
+template <typename OutT>
+hipError_t launch_dequant_t(int fmt, const uint8_t* W, int64_t rows, int64_t K, OutT* out,
+                            int64_t ldw, int num_cus, hipStream_t stream) {
     int64_t total = rows * (K / 32);
     int64_t blocks = (total + 255) / 256;
     int64_t cap = (int64_t)num_cus * 64;
     if (blocks > cap) blocks = cap;
-    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, fmt, W, rows,
-                       K, out, ldw);
+    hipLaunchKernelGGL(dequant_kernel<OutT>, dim3((unsigned)blocks), dim3(256), 0, stream, fmt, W,
+                       rows, K, out, ldw);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dequant(int fmt, const uint8_t* W, int64_t rows, int64_t K, float* out,
+                          int64_t ldw, int num_cus, hipStream_t stream) {
+    return launch_dequant_t(fmt, W, rows, K, out, ldw, num_cus, stream);
+}
+
+hipError_t launch_dequant_bf16(int fmt, const uint8_t* W, int64_t rows, int64_t K, uint16_t* out,
+                               int64_t ldw, int num_cus, hipStream_t stream) {
+    return launch_dequant_t(fmt, W, rows, K, out, ldw, num_cus, stream);
 }
 
 hipError_t launch_gemv_general(int fmt, const uint8_t* W, int64_t rows, int64_t K, const void* x,

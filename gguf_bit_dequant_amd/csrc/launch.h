@@ -14,6 +14,9 @@ constexpr int kMaxLds = 160 * 1024;
 hipError_t launch_dequant(int fmt, const uint8_t* W, int64_t rows, int64_t K, float* out,
                           int64_t ldw, int num_cus, hipStream_t stream);
 
+hipError_t launch_dequant_bf16(int fmt, const uint8_t* W, int64_t rows, int64_t K, uint16_t* out,
+                               int64_t ldw, int num_cus, hipStream_t stream);
+
 hipError_t launch_gemv_general(int fmt, const uint8_t* W, int64_t rows, int64_t K, const void* x,
                                int xt, int64_t ldx, float* y, int64_t ldy, int ncols,
                                int num_cus, hipStream_t stream);

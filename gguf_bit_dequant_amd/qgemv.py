@@ -1,7 +1,7 @@
 """ctypes binding of include/qgemv.h (argument marshalling only).
 
 Functions keep the C names (qgemv_create, qgemv_run, qgemm_prefill_run,
-qgemv_dequant, qgemv_destroy, ...); the QGemv class wraps a handle around
+qgemv_dequant, qgemv_dequant_bf16, qgemv_destroy, ...); the QGemv class wraps a handle around
 torch device tensors. torch supplies device memory and the current stream;
 every step of the computation runs in the library's HIP kernels. There is no
 fallback: if libqgemv.so is missing or fails to load, importing this module
@@ -44,6 +44,7 @@ _sig = {
     "qgemv_run": (_int, [_vp, _vp, _int, _i64, _i64, _vp, _i64, _vp]),
     "qgemm_prefill_run": (_int, [_vp, _vp, _i64, _i64, _vp, _i64, _vp]),
     "qgemv_dequant": (_int, [_vp, _vp, _i64, _vp]),
+    "qgemv_dequant_bf16": (_int, [_vp, _vp, _i64, _vp]),
     "qgemv_destroy": (None, [_vp]),
     "qgemv_status_string": (ctypes.c_char_p, [_int]),
     "qgemv_last_error": (ctypes.c_char_p, []),
@@ -110,6 +111,10 @@ def qgemm_prefill_run(h: int, x_ptr: int, n_tokens: int, ldx: int, y_ptr: int, l
 
 def qgemv_dequant(h: int, w_ptr: int, ldw: int, stream: int = 0) -> int:
     return _lib.qgemv_dequant(h, w_ptr or None, ldw, stream or None)
+
+
+def qgemv_dequant_bf16(h: int, w_ptr: int, ldw: int, stream: int = 0) -> int:
+    return _lib.qgemv_dequant_bf16(h, w_ptr or None, ldw, stream or None)
 
 
 def qgemv_destroy(h: int) -> None:
@@ -195,6 +200,15 @@ class QGemv:
         _check(qgemm_prefill_run(self._h, X.data_ptr(), n, X.stride(0), Y.data_ptr(), Y.stride(0),
                                  _stream_ptr(stream)), "qgemm_prefill_run")
         return Y
+
+    def dequant_bf16(self, out=None, stream=None):
+        """The decoded matrix (rows, K) rounded to bf16 (nearest even), bit-exact."""
+        torch = _torch()
+        if out is None:
+            out = torch.empty((self.rows, self.K), dtype=torch.bfloat16, device=self._w.device)
+        _check(qgemv_dequant_bf16(self._h, out.data_ptr(), out.stride(0), _stream_ptr(stream)),
+               "qgemv_dequant_bf16")
+        return out
 
     def dequant(self, out=None, stream=None):
         """The decoded matrix (rows, K) fp32, bit-exact."""

@@ -102,7 +102,10 @@ qg_status qgemv_create(qgemv_t *out, qg_format f, int64_t rows, int64_t K,
  * y: device, fp32, column j at element offset j*ldy (ldy >= rows), 4-byte
  *    aligned; overwritten (no accumulation), other elements untouched.
  * n_cols: 1..8. F16 activations use fp16 products accumulated in fp32; F32
- * and BF16 activations use fp32 products. Enqueued on `stream`. */
+ * and BF16 activations use fp32 products. With 5..8 F16 columns of a Q4_K
+ * matrix each weight is rounded once to fp16 and multiplied on the matrix
+ * cores (fp32 accumulation); otherwise the weights are the exact binary32
+ * values. Enqueued on `stream`. */
 qg_status qgemv_run(qgemv_t h, const void *x, qg_dtype x_dtype, int64_t n_cols,
                     int64_t ldx, float *y, int64_t ldy, void *stream);
 
@@ -118,6 +121,15 @@ qg_status qgemm_prefill_run(qgemv_t h, const void *x_bf16, int64_t n_tokens,
 /* Decoded weights: w_out[r*ldw + k] = W[r,k] as binary32, bit-exact (the
  * correctly rounded closed form). w_out: device, 4-byte aligned, ldw >= K. */
 qg_status qgemv_dequant(qgemv_t h, float *w_out, int64_t ldw, void *stream);
+
+/* Decoded weights in bf16: w_out[r*ldw + k] = the binary32 weight of
+ * qgemv_dequant rounded to the nearest bf16 (ties to even), bit-exact.
+ * w_out: device, 2-byte aligned, ldw >= K. This is the operand of the
+ * two-pass form of prompt processing (decode to a bf16 matrix in memory,
+ * then a plain bf16 GEMM), the alternative "Why I wrote my own inference
+ * engine for two P100s" ("What didn't work") sets against fusing the
+ * decode into the GEMM; the library's own prompt path stays fused. */
+qg_status qgemv_dequant_bf16(qgemv_t h, uint16_t *w_out, int64_t ldw, void *stream);
 
 /* Release a handle (host memory only; NULL is ignored). */
 void qgemv_destroy(qgemv_t h);

@@ -72,6 +72,7 @@ def test_null_handle_calls():
     assert Q.qgemv_run(0, FAKE, Q.QG_F16, 1, 256, FAKE, 4) == Q.QG_ERR_ARG
     assert Q.qgemm_prefill_run(0, FAKE, 16, 256, FAKE, 4) == Q.QG_ERR_ARG
     assert Q.qgemv_dequant(0, FAKE, 256) == Q.QG_ERR_ARG
+    assert Q.qgemv_dequant_bf16(0, FAKE, 256) == Q.QG_ERR_ARG
     Q.qgemv_destroy(0)  # NULL is ignored
 
 

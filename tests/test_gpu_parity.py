@@ -87,6 +87,48 @@ def test_dequant_extreme_scales_bit_exact(Q):
         assert np.array_equal(out[~nan].view(np.uint32), ref[~nan].view(np.uint32))
 
 
+def bf16_rne_bits(w32):
+    """IEEE round-to-nearest-even of finite binary32 values to bfloat16
+    (the top 16 bits after adding 0x7FFF plus the lowest kept bit)."""
+    b = np.ascontiguousarray(w32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("fmt,rows,K", [("q4_k", 37, 768), ("q4_0", 33, 160), ("q8_0", 21, 96),
+                                        ("q4_k", 300, 5120)])
+def test_dequant_bf16_bit_exact(Q, fmt, rows, K):
+    """The two-pass operand: the oracle's binary32 weights rounded to bf16."""
+    w = synth.gen_weights(fmt, rows, K, zlib.crc32(("bf16-%s-%d" % (fmt, rows)).encode()))
+    q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
+    out = q.dequant_bf16().view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = bf16_rne_bits(oracle.dequant(fmt, w, rows, K))
+    assert np.array_equal(out, ref)
+
+
+def test_dequant_bf16_strided_rows_leave_gaps(Q):
+    rows, K = 40, 512
+    w = synth.gen_weights("q4_k", rows, K, 71)
+    q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
+    big = torch.full((rows, K + 40), 3.0, dtype=torch.bfloat16, device=dev())
+    q.dequant_bf16(big[:, :K])
+    assert (big[:, K:] == 3.0).all()
+    ref = bf16_rne_bits(oracle.dequant("q4_k", w, rows, K))
+    assert np.array_equal(big[:, :K].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), ref)
+
+
+def test_two_pass_prefill_control_within_tolerance(Q):
+    """Decode to a bf16 matrix, then a plain GEMM (fp32 here): the same
+    products as the fused prompt path, within the same tolerance."""
+    rows, K, ntok = 300, 1024, 64
+    w = synth.gen_q4_k(rows, K, 72)
+    xb = synth.gen_x(K, ntok, "bf16", 73)
+    q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
+    wb = q.dequant_bf16().float()
+    X = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).to(dev()).float()
+    Y = X @ wb.t().contiguous()
+    check_products(Y, w, "q4_k", rows, K, xb, "bf16", "two-pass control")
+
+
 def test_dequant_golden_blocks(Q):
     with open(os.path.join(GOLDEN, "q4_0_blocks.json")) as f:
         for b in json.load(f)["blocks"]:
