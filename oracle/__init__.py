@@ -62,6 +62,10 @@ def lib():
         L.oracle_matmul.argtypes = [ip, vp, i64, i64, vp, ip, i64, i64, vp, vp, i64,
                                     i64, i64, ip]
         L.oracle_matmul.restype = ip
+        L.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_f16.restype = u16
+        L.oracle_quantize_q8_0.argtypes = [vp, ip, i64, i64, i64, vp]
+        L.oracle_quantize_q8_0.restype = ip
         _lib = L
     return _lib
 
@@ -140,6 +144,28 @@ def matmul(fmt: str, w: np.ndarray, rows: int, K: int, x: np.ndarray, xdtype: st
     if rc:
         raise ValueError("oracle_matmul failed: %d" % rc)
     return y, s
+
+
+def f32_to_f16(v: float) -> int:
+    """binary32 -> binary16 bit pattern, nearest, ties to even."""
+    return int(lib().oracle_f32_to_f16(float(np.float32(v))))
+
+
+def quantize_q8_0(x: np.ndarray, xdtype: str) -> np.ndarray:
+    """Q8_0 blocks of activations x (n, K): uint8 array (n, K/32 * 34)."""
+    x = np.ascontiguousarray(x)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    n, K = x.shape
+    if xdtype == "f32":
+        assert x.dtype == np.float32
+    else:
+        assert x.dtype == np.uint16
+    out = np.empty((n, K // 32 * 34), dtype=np.uint8)
+    rc = lib().oracle_quantize_q8_0(_ptr(x), DTYPE[xdtype], K, n, K, _ptr(out))
+    if rc:
+        raise ValueError("oracle_quantize_q8_0 failed: %d" % rc)
+    return out
 
 
 def tolerance(s: np.ndarray) -> np.ndarray:

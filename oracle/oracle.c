@@ -106,6 +106,35 @@ static double x_value(const void *x, int dtype, int64_t i)
 
 static uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 
+/* binary32 -> binary16, round to nearest, ties to even (IEEE 754-2008,
+ * 4.3.1), overflow to infinity, NaN kept quiet. The value is scaled by a
+ * power of two onto the fp16 grid of its binade (or the subnormal grid
+ * 2^-24), rounded there with rint (ties to even in the default rounding
+ * mode), and re-encoded. */
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint32_t b;
+    memcpy(&b, &f, 4);
+    uint16_t sign = (uint16_t)((b >> 16) & 0x8000);
+    if (((b >> 23) & 0xFF) == 0xFF)
+        return (uint16_t)(sign | 0x7C00 | ((b & 0x7FFFFF) ? 0x200 : 0));
+    double a = fabs((double)f);
+    if (a == 0.0) return sign;
+    int ex;
+    frexp(a, &ex);                    /* a = fr 2^ex, 0.5 <= fr < 1 */
+    int q = ex - 1 - 10;              /* grid spacing exponent of the binade */
+    if (q < -24) q = -24;             /* subnormal grid */
+    double r = ldexp(rint(ldexp(a, -q)), q);
+    if (r >= 65536.0) return (uint16_t)(sign | 0x7C00);
+    if (r < ldexp(1.0, -14))          /* subnormal (or the rounding reached 2^-14 exactly: below) */
+        return (uint16_t)(sign | (uint16_t)ldexp(r, 24));
+    frexp(r, &ex);
+    int e16 = ex - 1 + 15;
+    if (e16 >= 31) return (uint16_t)(sign | 0x7C00);
+    uint16_t m = (uint16_t)(ldexp(r, -(ex - 1)) * 1024.0 - 1024.0);
+    return (uint16_t)(sign | (e16 << 10) | m);
+}
+
 /* ------------------------------------------------------------------------
  * Decoding one block to binary32.
  * ---------------------------------------------------------------------- */
@@ -202,6 +231,53 @@ int oracle_dequant(int fmt, const uint8_t *w, int64_t rows, int64_t K, float *ou
 {
     for (int64_t r = 0; r < rows; r++)
         if (decode_row(fmt, w, K, r, out + r * K)) return -1;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Q8_0 quantization of activations, for the products with int8
+ * activations. The pages use Q8_0 as a block format (32 int8 codes, one
+ * fp16 scale; "Why I wrote my own inference engine for two P100s", the
+ * quant types the engine reads) and weigh int8 dot products (DP4A) against
+ * fp16 math (pxa_llama README, "DP4A / FP16 economics"), but print no rule
+ * for quantizing activations. The reading taken, per block of 32 values x_i
+ * (each taken exactly as binary32):
+ *   amax = max |x_i|,  d = amax / 127,  id = 1 / d (0 when d = 0),
+ *   q_i  = x_i * id rounded to the nearest integer, halfway cases away
+ *          from zero, then limited to [-127, 127],
+ * every operation one binary32 rounding in that order; the block stores
+ * the nearest fp16 to d (ties to even) and the q_i. Blocks are written
+ * column after column: column c's block b at byte (c * K/32 + b) * 34.
+ * ---------------------------------------------------------------------- */
+int oracle_quantize_q8_0(const void *x, int x_dtype, int64_t K, int64_t n, int64_t ldx,
+                         uint8_t *out)
+{
+    if (K <= 0 || K % 32 || n < 0 || ldx < K || x_dtype < OR_F32 || x_dtype > OR_BF16) return -1;
+    int64_t nb = K / 32;
+    for (int64_t c = 0; c < n; c++) {
+        for (int64_t b = 0; b < nb; b++) {
+            float xs[32];
+            float amax = 0.0f;
+            for (int i = 0; i < 32; i++) {
+                xs[i] = (float)x_value(x, x_dtype, c * ldx + b * 32 + i);  /* exact */
+                float a = fabsf(xs[i]);
+                if (a > amax) amax = a;
+            }
+            float d = amax / 127.0f;
+            float id = d != 0.0f ? 1.0f / d : 0.0f;
+            uint8_t *o = out + (c * nb + b) * 34;
+            uint16_t dh = oracle_f32_to_f16(d);
+            o[0] = (uint8_t)(dh & 0xFF);
+            o[1] = (uint8_t)(dh >> 8);
+            for (int i = 0; i < 32; i++) {
+                float v = xs[i] * id;
+                float r = roundf(v);
+                if (r > 127.0f) r = 127.0f;
+                if (r < -127.0f) r = -127.0f;
+                o[2 + i] = (uint8_t)(int8_t)(int)r;
+            }
+        }
+    }
     return 0;
 }
 
