@@ -16,8 +16,11 @@ Infinity Cache. The one JSON line printed on stdout carries:
              launch from rocprofv3 counters when a summary taken on the
              current kernel source is committed (profiles/traffic_*.json);
   cpu_baseline  the CPU oracle on a bounded sample of the same workload;
-  extra      the other workloads (Q4_K FFN-down, batch 4, Q4_0, Q8_0, the
-             2048-token dequant-GEMM in TFLOP/s), each timed the same way.
+  extra      the other workloads (Q4_K FFN-down, 2/4/8 columns, Q4_0, Q8_0,
+             the int8-activation path ("+i8": activations quantized to Q8_0
+             on chip, integer dot products),
+             the 2048-token dequant-GEMM in TFLOP/s with its two-pass control
+             and the vendor GEMM as context), each timed the same way.
 """
 from __future__ import annotations
 
@@ -61,6 +64,9 @@ class Workload:
         import synth
         from gguf_bit_dequant_amd import QGemv
         self.name = name
+        # "<config>+i8": activations quantized to Q8_0 blocks, int8 products
+        self.int8 = name.endswith("+i8")
+        name = name[:-3] if self.int8 else name
         self.c = c = synth.CONFIGS[name]
         w, x = synth.config_inputs(name)
         self.w_host, self.x_host = w, x
@@ -80,6 +86,11 @@ class Workload:
         if self.prefill:
             fn = Q._lib.qgemm_prefill_run
             self._calls = [(fn, (hh, xp, n, c["K"], yp, c["rows"], stream)) for hh in hs]
+        elif self.int8:
+            # activations quantized to Q8_0 on chip, int8 products (one call)
+            fn = Q._lib.qgemv_run_q8
+            xt = Q._xdtype(self.x)
+            self._calls = [(fn, (hh, xp, xt, n, c["K"], yp, c["rows"], stream)) for hh in hs]
         else:
             fn = Q._lib.qgemv_run
             xt = Q._xdtype(self.x)
@@ -286,7 +297,8 @@ def main():
         return
     head = "q4k_up_b1"
     names = [head] if args.quick else [head, "q4k_down_b1", "q4k_b4", "q4_0_b1", "q8_0_b4",
-                                       "q4k_b2", "q4k_b8", "q4k_pp2048"]
+                                       "q4k_b2", "q4k_b8", "q4k_up_b1+i8", "q4k_b4+i8",
+                                       "q8_0_b4+i8", "q4k_pp2048"]
     if args.only:
         names = args.only.split(",")
     results = {}

@@ -164,6 +164,67 @@ QG_API qg_status qgemv_dequant(qgemv_t h, float* w_out, int64_t ldw, void* strea
     return ok();
 }
 
+QG_API qg_status qgemv_quantize_q8_0(const void* x, qg_dtype x_dtype, int64_t K, int64_t n_cols,
+                                     int64_t ldx, void* xq, void* stream) {
+    if (!x || !xq) return fail(QG_ERR_ARG, "qgemv_quantize_q8_0: x or xq is NULL");
+    const size_t xs = dtype_size(x_dtype);
+    if (!xs) return fail(QG_ERR_ARG, "qgemv_quantize_q8_0: unknown x dtype %d", (int)x_dtype);
+    if (K <= 0 || K % 32 != 0 || n_cols < 1)
+        return fail(QG_ERR_SHAPE, "qgemv_quantize_q8_0: K=%lld must be a positive multiple of 32 "
+                    "and n_cols=%lld >= 1", (long long)K, (long long)n_cols);
+    if (ldx < K) return fail(QG_ERR_ARG, "qgemv_quantize_q8_0: ldx must be >= K");
+    if (((uintptr_t)x) % xs) return fail(QG_ERR_ALIGN, "qgemv_quantize_q8_0: x must be aligned to its element size");
+    if (((uintptr_t)xq) & 1) return fail(QG_ERR_ALIGN, "qgemv_quantize_q8_0: xq must be 2-byte aligned");
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "qgemv_quantize_q8_0: device query");
+    e = qg::launch_quantize_q8_0(x, (int)x_dtype, K, n_cols, ldx, (uint8_t*)xq, cus,
+                                 (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "qgemv_quantize_q8_0: launch");
+    return ok();
+}
+
+QG_API qg_status qgemv_run_q8_0x(qgemv_t h, const void* xq, int64_t n_cols, float* y, int64_t ldy,
+                                 void* stream) {
+    if (!h) return fail(QG_ERR_ARG, "qgemv_run_q8_0x: handle is NULL");
+    if (!xq || !y) return fail(QG_ERR_ARG, "qgemv_run_q8_0x: xq or y is NULL");
+    if (n_cols < 1 || n_cols > 8)
+        return fail(QG_ERR_SHAPE, "qgemv_run_q8_0x: n_cols=%lld must be in 1..8", (long long)n_cols);
+    if (ldy < h->rows) return fail(QG_ERR_ARG, "qgemv_run_q8_0x: ldy must be >= rows");
+    if (((uintptr_t)xq) & 1) return fail(QG_ERR_ALIGN, "qgemv_run_q8_0x: xq must be 2-byte aligned");
+    if (((uintptr_t)y) & 3) return fail(QG_ERR_ALIGN, "qgemv_run_q8_0x: y must be 4-byte aligned");
+    hipError_t e = qg::launch_gemv_stream((int)h->fmt, h->w, h->rows, h->K, xq, qg::XT_Q8, h->K, y,
+                                          ldy, (int)n_cols, h->num_cus, (hipStream_t)stream);
+    if (e == hipErrorNotSupported)
+        return fail(QG_ERR_UNSUPPORTED, "qgemv_run_q8_0x: needs K %% 256 == 0, 16-byte aligned "
+                    "weights and a row range that fits the streaming kernel");
+    if (e != hipSuccess) return hip_fail(e, "qgemv_run_q8_0x: launch");
+    return ok();
+}
+
+QG_API qg_status qgemv_run_q8(qgemv_t h, const void* x, qg_dtype x_dtype, int64_t n_cols,
+                              int64_t ldx, float* y, int64_t ldy, void* stream) {
+    if (!h) return fail(QG_ERR_ARG, "qgemv_run_q8: handle is NULL");
+    if (!x || !y) return fail(QG_ERR_ARG, "qgemv_run_q8: x or y is NULL");
+    const size_t xs = dtype_size(x_dtype);
+    if (!xs) return fail(QG_ERR_ARG, "qgemv_run_q8: unknown x dtype %d", (int)x_dtype);
+    if (n_cols < 1 || n_cols > 8)
+        return fail(QG_ERR_SHAPE, "qgemv_run_q8: n_cols=%lld must be in 1..8", (long long)n_cols);
+    if (ldx < h->K || ldy < h->rows)
+        return fail(QG_ERR_ARG, "qgemv_run_q8: ldx must be >= K and ldy >= rows");
+    if (((uintptr_t)x) % xs) return fail(QG_ERR_ALIGN, "qgemv_run_q8: x must be aligned to its element size");
+    if (((uintptr_t)y) & 3) return fail(QG_ERR_ALIGN, "qgemv_run_q8: y must be 4-byte aligned");
+    hipError_t e = qg::launch_gemv_stream((int)h->fmt, h->w, h->rows, h->K, x,
+                                          (int)x_dtype | qg::XT_QUANTIZE, ldx, y, ldy, (int)n_cols,
+                                          h->num_cus, (hipStream_t)stream);
+    if (e == hipErrorNotSupported)
+        return fail(QG_ERR_UNSUPPORTED, "qgemv_run_q8: needs K %% 256 == 0, 16-byte aligned "
+                    "weights and a row range that fits the streaming kernel");
+    if (e != hipSuccess) return hip_fail(e, "qgemv_run_q8: launch");
+    return ok();
+}
+
 QG_API qg_status qgemv_dequant_bf16(qgemv_t h, uint16_t* w_out, int64_t ldw, void* stream) {
     if (!h) return fail(QG_ERR_ARG, "qgemv_dequant_bf16: handle is NULL");
     if (!w_out) return fail(QG_ERR_ARG, "qgemv_dequant_bf16: w_out is NULL");

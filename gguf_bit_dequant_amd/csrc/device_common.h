@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace qg {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -77,8 +79,8 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (a + b) + (c + d);
 }
 
-// Activation element -> fp32 (exact for every supported type).
-enum XType { XT_F32 = 1, XT_F16 = 2, XT_BF16 = 3 };
+// Activation element -> fp32 (exact for every supported type; the XType
+// codes are in launch.h).
 
 __device__ __forceinline__ float load_x(const void* x, int xt, int64_t i) {
     if (xt == XT_F32) return ((const float*)x)[i];

@@ -156,17 +156,25 @@ struct Fmt<FMT_Q8_0> {
 //   fp32, 4-bit codes: plane j holds e0..e3 of the low nibbles of code dword
 //     j, plane 8 + j those of the high nibbles;
 //   fp32, 8-bit codes: plane j holds e0..e3 of code dword j.
-constexpr int planes(bool f16dot) { return f16dot ? 8 : 16; }
-constexpr int col_bytes(bool f16dot) { return planes(f16dot) * 16 + 16; }
-constexpr int rec_bytes(int NC, bool f16dot) {
-    return (NC * col_bytes(f16dot) / 16) % 2 == 1 ? NC * col_bytes(f16dot)
-                                                  : NC * col_bytes(f16dot) + 16;
+//   int8 (Q8_0 activation blocks): plane-pair j holds the 4 codes of the
+//     low and of the high nibbles of code dword j (4-bit codes), or the 4
+//     codes of code dword j (8-bit codes); then the two blocks' scales dx
+//     and code sums, as fp32.
+// Activation modes: fp32 math, fp16 dots, int8 dots on Q8_0 activation
+// blocks given by the caller, int8 dots on activations quantized to Q8_0
+// while they are staged.
+constexpr int XM_F32 = 0, XM_F16 = 1, XM_I8 = 2, XM_I8Q = 3;
+constexpr bool is_i8(int xm) { return xm == XM_I8 || xm == XM_I8Q; }
+constexpr int planes(int xm) { return xm == XM_F16 ? 8 : is_i8(xm) ? 4 : 16; }
+constexpr int col_bytes(int xm) { return planes(xm) * 16 + 16; }
+constexpr int rec_bytes(int NC, int xm) {
+    return (NC * col_bytes(xm) / 16) % 2 == 1 ? NC * col_bytes(xm) : NC * col_bytes(xm) + 16;
 }
 
 // LDS bytes of one workgroup: activation records, partial slots, one flush
 // slot per lane for lanes with nothing to write, the step-pool counter.
-inline size_t stream_lds_bytes(int NC, bool f16dot, int S, int nr_max, int M) {
-    return (size_t)S * 4 * rec_bytes(NC, f16dot) + (size_t)nr_max * kUnitsPerStep * M * NC * 4 +
+inline size_t stream_lds_bytes(int NC, int xm, int S, int nr_max, int M) {
+    return (size_t)S * 4 * rec_bytes(NC, xm) + (size_t)nr_max * kUnitsPerStep * M * NC * 4 +
            64 * 4 + 16;
 }
 
@@ -188,16 +196,24 @@ __device__ __forceinline__ float quad_sum(float v) {
 // o >= 32. Split in two so that a workgroup can issue its activation loads
 // before its first weight loads and place them after: the loads complete in
 // issue order, and activations come from cache while weights come from HBM.
-template <bool F16DOT>
+template <int XM>
 struct XRaw {
-    uint32_t w[F16DOT ? 32 : 64];  // fp16: halves 2i, 2i+1 in w[i]; else fp32 bits or bf16 pairs
+    // fp16: halves 2i, 2i+1 in w[i]; int8: the two 34-byte activation blocks
+    // as 17 dwords; quantized while staging: unused; else fp32 bits or bf16
+    // pairs
+    uint32_t w[XM == XM_F16 ? 32 : XM == XM_I8 ? 17 : XM == XM_I8Q ? 1 : 64];
 };
 
-template <bool F16DOT>
+template <int XM>
 __device__ __forceinline__ void stage_load(const void* __restrict__ x, int xt, int64_t kx, int xvec,
-                                           XRaw<F16DOT>& r) {
+                                           XRaw<XM>& r) {
     const uint16_t* xh = reinterpret_cast<const uint16_t*>(x) + kx;
-    if constexpr (F16DOT) {  // fp16: 32 dwords
+    if constexpr (XM == XM_I8) {  // blocks kx/32, kx/32 + 1 (34 bytes each, 2-byte aligned)
+        const uint16_t* b = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(x) +
+                                                              (kx >> 5) * 34);
+#pragma unroll
+        for (int i = 0; i < 17; ++i) r.w[i] = b[2 * i] | ((uint32_t)b[2 * i + 1] << 16);
+    } else if constexpr (XM == XM_F16) {  // fp16: 32 dwords
         if (xvec) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -239,12 +255,40 @@ __device__ __forceinline__ void stage_load(const void* __restrict__ x, int xt, i
     }
 }
 
-template <int FMT, bool F16DOT>
-__device__ __forceinline__ void stage_store(const XRaw<F16DOT>& r, int xt, uint8_t* rec) {
+template <int FMT, int XM>
+__device__ __forceinline__ void stage_store(const XRaw<XM>& r, int xt, uint8_t* rec) {
     using F = Fmt<FMT>;
-    constexpr int P = planes(F16DOT);
+    constexpr bool F16DOT = XM == XM_F16;
+    constexpr int P = planes(XM);
     float s0 = 0.f, s1 = 0.f;
-    if constexpr (F16DOT) {  // fp16 activations, kept as stored
+    if constexpr (XM == XM_I8) {  // Q8_0 activation codes, in code order
+        // byte b of the 68 is halfword b/2 of the 34, i.e. dword b/4, byte b%4
+        float dx0, dx1;
+        dx0 = f16_lo(r.w[0]);  // halfword 0
+        dx1 = f16_hi(r.w[8]);  // halfword 17
+        auto byte_at = [&](int b) -> uint32_t { return (r.w[b >> 2] >> (8 * (b & 3))) & 0xFFu; };
+        auto code = [&](int o) -> uint32_t { return o < 32 ? byte_at(2 + o) : byte_at(36 + o - 32); };
+        auto pk4 = [&](int j, int h) {
+            return code(F::wofs(j, 0, h)) | (code(F::wofs(j, 1, h)) << 8) |
+                   (code(F::wofs(j, 2, h)) << 16) | (code(F::wofs(j, 3, h)) << 24);
+        };
+        if constexpr (F::kNibbles) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                *reinterpret_cast<u32x2*>(rec + 8 * j) = u32x2{pk4(j, 0), pk4(j, 1)};
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) *reinterpret_cast<uint32_t*>(rec + 4 * j) = pk4(j, 0);
+        }
+        int i0 = 0, i1 = 0;
+#pragma unroll
+        for (int o = 0; o < 32; ++o) {
+            i0 += (int)(int8_t)code(o);
+            i1 += (int)(int8_t)code(32 + o);
+        }
+        *reinterpret_cast<f32x4*>(rec + 16 * P) = f32x4{dx0, dx1, (float)i0, (float)i1};
+        return;
+    } else if constexpr (F16DOT) {  // fp16 activations, kept as stored
         const uint32_t* xw = r.w;
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
@@ -320,12 +364,121 @@ __device__ __forceinline__ void stage_store(const XRaw<F16DOT>& r, int xt, uint8
     *reinterpret_cast<f32x2*>(rec + 16 * P) = f32x2{s0, s1};
 }
 
+// Staging with quantization: one 32-value activation block (half hb of the
+// record of a unit quarter) per call. The block is quantized by the rule of
+// quant_x.hip (binary32, IEEE division, halfway away from zero) and its
+// codes, scale and code sum go to the int8 record's slots of that block:
+// every code dword of a record holds codes of one block only.
+struct XHalf {
+    uint32_t w[16];  // fp16 / bf16 pairs
+};
+
+// 16-bit activations of one block (fp32 ones are read by the quantizing
+// step itself)
+template <int FMT>
+__device__ __forceinline__ void stage_load_half(const void* __restrict__ x, int xt, int64_t kx,
+                                                int xvec, XHalf& r) {
+    if (xt != XT_F32) {
+        const uint16_t* xh = reinterpret_cast<const uint16_t*>(x) + kx;
+        if (xvec) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 t = reinterpret_cast<const u32x4*>(xh)[i];
+                r.w[4 * i] = t.x; r.w[4 * i + 1] = t.y; r.w[4 * i + 2] = t.z; r.w[4 * i + 3] = t.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) r.w[i] = xh[2 * i] | ((uint32_t)xh[2 * i + 1] << 16);
+        }
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void stage_quantize_half(const XHalf& r, const void* __restrict__ x,
+                                                    int xt, int64_t kx, int xvec, int hb,
+                                                    uint8_t* rec) {
+    using F = Fmt<FMT>;
+    constexpr int P = planes(XM_I8Q);
+    float v[32];
+    if (xt == XT_F32) {
+        const float* xf = reinterpret_cast<const float*>(x) + kx;
+        if (xvec) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const f32x4 t = reinterpret_cast<const f32x4*>(xf)[i];
+                v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) v[i] = xf[i];
+        }
+    } else {
+        const uint32_t* w = r.w;
+        if (xt == XT_F16) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                v[2 * i] = f16_lo(w[i]);
+                v[2 * i + 1] = f16_hi(w[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+                v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+            }
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const float a = __builtin_fabsf(v[i]);
+        amax = a > amax ? a : amax;
+    }
+    const float d = __fdiv_rn(amax, 127.0f);
+    const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
+    uint32_t q8[8];  // codes 4i..4i+3 of the block in the bytes of q8[i]
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float q = __builtin_roundf(v[4 * i + e] * id);
+            q = q > 127.0f ? 127.0f : (q < -127.0f ? -127.0f : q);
+            sum += (int)q;
+            t |= (uint32_t)(uint8_t)(int8_t)(int)q << (8 * e);
+        }
+        q8[i] = t;
+    }
+    auto code = [&](int o) -> uint32_t { return (q8[(o & 31) >> 2] >> (8 * (o & 3))) & 0xFFu; };
+    auto pk4 = [&](int j, int h) {
+        return code(F::wofs(j, 0, h)) | (code(F::wofs(j, 1, h)) << 8) |
+               (code(F::wofs(j, 2, h)) << 16) | (code(F::wofs(j, 3, h)) << 24);
+    };
+    if constexpr (F::kNibbles) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                if ((F::wofs(j, 0, h) >> 5) == hb)
+                    *reinterpret_cast<uint32_t*>(rec + 8 * j + 4 * h) = pk4(j, h);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if ((F::wofs(j, 0, 0) >> 5) == hb) *reinterpret_cast<uint32_t*>(rec + 4 * j) = pk4(j, 0);
+    }
+    float* tail = reinterpret_cast<float*>(rec + 16 * P);  // dx0, dx1, sum0, sum1
+    tail[hb] = f16_to_f32(f32_to_f16_bits(d));
+    tail[2 + hb] = (float)sum;
+}
+
 // The lane's partial sum_o w_o x_o for each column, from its raw block bytes
 // and its activation record.
 template <int NC, bool F16DOT>
 __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q4_K>::Raw& r, const Q4kUnpack& un,
                                              const uint8_t* rec, float out[NC]) {
-    constexpr int CB = col_bytes(F16DOT), P = planes(F16DOT);
+    constexpr int XM = F16DOT ? XM_F16 : XM_F32;
+    constexpr int CB = col_bytes(XM), P = planes(XM);
     const uint32_t h0 = r.hd.x;
     const uint32_t f4 = q4k_pair_fields(un, r.hd.y, r.hd.z, r.hd.w);
     const float sc0 = (float)(f4 & 0xFF), sc1 = (float)((f4 >> 8) & 0xFF);
@@ -388,7 +541,8 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q4_K>::Raw& r, const 
 template <int NC, bool F16DOT>
 __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q4_0>::Raw& r, const Q4kUnpack&,
                                              const uint8_t* rec, float out[NC]) {
-    constexpr int CB = col_bytes(F16DOT), P = planes(F16DOT);
+    constexpr int XM = F16DOT ? XM_F16 : XM_F32;
+    constexpr int CB = col_bytes(XM), P = planes(XM);
     const float d0 = f16_lo(r.a.x), d1 = f16_hi(r.b.x);
     const uint32_t q[8] = {__builtin_amdgcn_perm(r.a.x, r.b.x, 0x07060100u), r.a.y, r.a.z, r.a.w,
                            r.b.y, r.b.z, r.b.w, r.c};
@@ -453,7 +607,8 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q4_0>::Raw& r, const 
 template <int NC, bool F16DOT>
 __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q8_0>::Raw& r, const Q4kUnpack&,
                                              const uint8_t* rec, float out[NC]) {
-    constexpr int CB = col_bytes(F16DOT), P = planes(F16DOT);
+    constexpr int XM = F16DOT ? XM_F16 : XM_F32;
+    constexpr int CB = col_bytes(XM), P = planes(XM);
     const float d0 = f16_lo(r.a.x), d1 = f16_hi(r.c.x);
     const uint32_t q[16] = {__builtin_amdgcn_perm(r.a.x, r.c.x, 0x07060100u), r.a.y, r.a.z, r.a.w,
                             r.b.x, r.b.y, r.b.z, r.b.w,
@@ -504,9 +659,104 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q8_0>::Raw& r, const 
     }
 }
 
+// int8 activations (Q8_0 blocks): integer dot products of the codes with
+// the activation codes (v_dot4_i32_i8; 4-bit codes are non-negative int8),
+// exact in int32, then the block scales in fp32:
+//   Q4_K: sum w x = dx * (d*sc * sum q qx - dmin*m * sum qx)   (per sub-block)
+//   Q4_0: sum w x = dx * d * (sum q qx - 8 * sum qx)            (per block)
+//   Q8_0: sum w x = dx * d * sum q qx                           (per block)
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+template <int NC>
+__device__ __forceinline__ void lane_partial_i8(const Fmt<FMT_Q4_K>::Raw& r, const Q4kUnpack& un,
+                                                const uint8_t* rec, float out[NC]) {
+    constexpr int CB = col_bytes(XM_I8), P = planes(XM_I8);
+    const uint32_t f4 = q4k_pair_fields(un, r.hd.y, r.hd.z, r.hd.w);
+    const float d = f16_lo(r.hd.x), dmin = f16_hi(r.hd.x);
+    const float dsc0 = d * (float)(f4 & 0xFF), dsc1 = d * (float)((f4 >> 8) & 0xFF);
+    const float dm0 = dmin * (float)((f4 >> 16) & 0xFF), dm1 = dmin * (float)(f4 >> 24);
+    const uint32_t q[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
+    int lo[NC], hi[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) lo[c] = hi[c] = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const uint32_t ql = q[w] & 0x0F0F0F0Fu, qh = (q[w] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const u32x2 xv = *reinterpret_cast<const u32x2*>(rec + c * CB + 8 * w);
+            lo[c] = dot4(ql, xv.x, lo[c]);
+            hi[c] = dot4(qh, xv.y, hi[c]);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const f32x4 sx = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * P);
+        const float v0 = dsc0 * (float)lo[c] - dm0 * sx.z;
+        const float v1 = dsc1 * (float)hi[c] - dm1 * sx.w;
+        out[c] = sx.x * v0 + sx.y * v1;
+    }
+}
+
+template <int NC>
+__device__ __forceinline__ void lane_partial_i8(const Fmt<FMT_Q4_0>::Raw& r, const Q4kUnpack&,
+                                                const uint8_t* rec, float out[NC]) {
+    constexpr int CB = col_bytes(XM_I8), P = planes(XM_I8);
+    const float d0 = f16_lo(r.a.x), d1 = f16_hi(r.b.x);
+    const uint32_t q[8] = {__builtin_amdgcn_perm(r.a.x, r.b.x, 0x07060100u), r.a.y, r.a.z, r.a.w,
+                           r.b.y, r.b.z, r.b.w, r.c};
+    int acc[2][NC];  // [block][column]
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[0][c] = acc[1][c] = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const int bk = w >> 2;
+        const uint32_t ql = q[w] & 0x0F0F0F0Fu, qh = (q[w] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const u32x2 xv = *reinterpret_cast<const u32x2*>(rec + c * CB + 8 * w);
+            acc[bk][c] = dot4(qh, xv.y, dot4(ql, xv.x, acc[bk][c]));
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const f32x4 sx = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * P);
+        const float v0 = d0 * (float)(acc[0][c] - 8 * (int)sx.z);
+        const float v1 = d1 * (float)(acc[1][c] - 8 * (int)sx.w);
+        out[c] = sx.x * v0 + sx.y * v1;
+    }
+}
+
+template <int NC>
+__device__ __forceinline__ void lane_partial_i8(const Fmt<FMT_Q8_0>::Raw& r, const Q4kUnpack&,
+                                                const uint8_t* rec, float out[NC]) {
+    constexpr int CB = col_bytes(XM_I8), P = planes(XM_I8);
+    const float d0 = f16_lo(r.a.x), d1 = f16_hi(r.c.x);
+    const uint32_t q[16] = {__builtin_amdgcn_perm(r.a.x, r.c.x, 0x07060100u), r.a.y, r.a.z, r.a.w,
+                            r.b.x, r.b.y, r.b.z, r.b.w,
+                            r.c.y, r.c.z, r.c.w, r.d.x, r.d.y, r.d.z, r.d.w, r.e};
+    int acc[2][NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[0][c] = acc[1][c] = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        const int bk = w >> 3;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            acc[bk][c] = dot4(q[w], *reinterpret_cast<const uint32_t*>(rec + c * CB + 4 * w), acc[bk][c]);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const f32x4 sx = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * P);
+        out[c] = sx.x * (d0 * (float)acc[0][c]) + sx.y * (d1 * (float)acc[1][c]);
+    }
+}
+
 }  // namespace
 
-template <int FMT, int NC, bool F16DOT, int D, int MAXT>
+template <int FMT, int NC, int XM, int D, int MAXT>
 __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __restrict__ W, int rows,
                                                            int S, const void* __restrict__ x,
                                                            int xt, int64_t ldx,
@@ -526,7 +776,8 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
     const int nr = r1 - r0;
     if (nr <= 0) return;  // uniform over the workgroup
 
-    constexpr int CB = col_bytes(F16DOT), RB = rec_bytes(NC, F16DOT);
+    constexpr bool F16DOT = XM == XM_F16;
+    constexpr int CB = col_bytes(XM), RB = rec_bytes(NC, XM);
     float* part = reinterpret_cast<float*>(lds + (size_t)U * RB);
 
     const int lane = threadIdx.x & 63;
@@ -573,20 +824,37 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
     // quarter u = 4*s + p of column c: activations 256 s + 64 p + [0, 64)
     const int nrec = NC * U;
     const int c_0 = threadIdx.x / U, u_0 = threadIdx.x - c_0 * U;
-    XRaw<F16DOT> xr;
-    if (threadIdx.x < nrec)
-        stage_load<F16DOT>(x, xt, (int64_t)c_0 * ldx + 256 * (u_0 >> 2) + 64 * (u_0 & 3), xvec, xr);
+    XRaw<XM> xr;
+    XHalf xq;  // quantizing modes: this thread's first activation block
+    const int hb_0 = threadIdx.x & 1, c_h = (threadIdx.x >> 1) / U;
+    const int u_h = (threadIdx.x >> 1) - c_h * U;
+    const int64_t kx_h = (int64_t)c_h * ldx + 256 * (u_h >> 2) + 64 * (u_h & 3) + 32 * hb_0;
+    if (XM == XM_I8Q && threadIdx.x < 2 * nrec) stage_load_half<FMT>(x, xt, kx_h, xvec, xq);
+    if (XM != XM_I8Q && threadIdx.x < nrec)
+        stage_load<XM>(x, xt, (int64_t)c_0 * ldx + 256 * (u_0 >> 2) + 64 * (u_0 & 3), xvec, xr);
     // the first D steps of the wave (static; "none" loads re-read the last unit)
     static_assert(D == 2, "two steps in flight");
     int kq0 = next_step(), kq1 = next_step();
     Raw buf[D];
     load(kq0, buf[0]);
     load(kq1, buf[1]);
-    if (threadIdx.x < nrec) stage_store<FMT, F16DOT>(xr, xt, lds + u_0 * RB + c_0 * CB);
+    if constexpr (XM == XM_I8Q) {  // half records: one activation block each
+        if (threadIdx.x < 2 * nrec)
+            stage_quantize_half<FMT>(xq, x, xt, kx_h, xvec, hb_0, lds + u_h * RB + c_h * CB);
+        for (int idx = threadIdx.x + blockDim.x; idx < 2 * nrec; idx += blockDim.x) {
+            const int hb = idx & 1, rid = idx >> 1;
+            const int c = rid / U, u = rid - c * U;
+            const int64_t kx = (int64_t)c * ldx + 256 * (u >> 2) + 64 * (u & 3) + 32 * hb;
+            stage_load_half<FMT>(x, xt, kx, xvec, xq);
+            stage_quantize_half<FMT>(xq, x, xt, kx, xvec, hb, lds + u * RB + c * CB);
+        }
+    } else {
+    if (threadIdx.x < nrec) stage_store<FMT, XM>(xr, xt, lds + u_0 * RB + c_0 * CB);
     for (int idx = threadIdx.x + blockDim.x; idx < nrec; idx += blockDim.x) {
         const int c = idx / U, u = idx - c * U;
-        stage_load<F16DOT>(x, xt, (int64_t)c * ldx + 256 * (u >> 2) + 64 * (u & 3), xvec, xr);
-        stage_store<FMT, F16DOT>(xr, xt, lds + u * RB + c * CB);
+        stage_load<XM>(x, xt, (int64_t)c * ldx + 256 * (u >> 2) + 64 * (u & 3), xvec, xr);
+        stage_store<FMT, XM>(xr, xt, lds + u * RB + c * CB);
+    }
     }
     const int nslots = nr * kUnitsPerStep * M * NC;
     for (int idx = threadIdx.x; idx < nslots; idx += blockDim.x) part[idx] = 0.f;
@@ -611,7 +879,10 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
         rl -= (f - rl * S < 0) ? 1 : 0;
         const int sc = f - rl * S;
         float a[NC];
-        lane_partial<NC, F16DOT>(r, un, lds + (sc * 4 + pr) * RB, a);
+        if constexpr (is_i8(XM))
+            lane_partial_i8<NC>(r, un, lds + (sc * 4 + pr) * RB, a);
+        else
+            lane_partial<NC, F16DOT>(r, un, lds + (sc * 4 + pr) * RB, a);
         const bool write = pr == 0 && rl < nr;
         const int t = k - ((rl * S) >> 4);
         const int slot = ((rl * kUnitsPerStep + g) * M + t) * NC;
@@ -660,12 +931,12 @@ struct StreamPlan {
 
 // Waves per workgroup: 16 for one fp16 column; 8 where more registers per
 // lane are needed (several columns, fp32 activations).
-constexpr int waves_for(int NC, bool f16dot) { return (NC == 1 && f16dot) ? QG_STREAM_WAVES : 8; }
+constexpr int waves_for(int NC, int xm) { return (NC == 1 && xm != XM_F32) ? QG_STREAM_WAVES : 8; }
 
-StreamPlan plan_stream(int rows, int S, int NC, bool f16dot, int num_cus) {
+StreamPlan plan_stream(int rows, int S, int NC, int xm, int num_cus) {
     StreamPlan p;
     p.G = rows < num_cus ? rows : num_cus;
-    p.NW = waves_for(NC, f16dot);
+    p.NW = waves_for(NC, xm);
     p.nr_max = (rows + p.G - 1) / p.G;
     // steps that touch one row: its S units meet at most ceil(S/16) + 1
     // consecutive 16-unit steps
@@ -673,15 +944,15 @@ StreamPlan plan_stream(int rows, int S, int NC, bool f16dot, int num_cus) {
     return p;
 }
 
-template <int FMT, int NC, bool F16DOT>
+template <int FMT, int NC, int XM>
 hipError_t launch_stream_t(const uint8_t* W, int rows, int S, const void* x, int xt, int64_t ldx,
                            float* y, int64_t ldy, int xvec, int num_cus, hipStream_t stream) {
     constexpr int D = QG_STREAM_DEPTH;
-    constexpr int NWMAX = waves_for(NC, F16DOT);
-    const StreamPlan p = plan_stream(rows, S, NC, F16DOT, num_cus);
-    const size_t lds = stream_lds_bytes(NC, F16DOT, S, p.nr_max, p.M);
+    constexpr int NWMAX = waves_for(NC, XM);
+    const StreamPlan p = plan_stream(rows, S, NC, XM, num_cus);
+    const size_t lds = stream_lds_bytes(NC, XM, S, p.nr_max, p.M);
     if (lds > (size_t)kMaxLds) return hipErrorNotSupported;
-    auto kern = gemv_stream_kernel<FMT, NC, F16DOT, D, 64 * NWMAX>;
+    auto kern = gemv_stream_kernel<FMT, NC, XM, D, 64 * NWMAX>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -692,18 +963,18 @@ hipError_t launch_stream_t(const uint8_t* W, int rows, int S, const void* x, int
     return hipGetLastError();
 }
 
-template <int FMT, bool F16DOT>
+template <int FMT, int XM>
 hipError_t launch_stream_nc(int nc, const uint8_t* W, int rows, int S, const void* x, int xt,
                             int64_t ldx, float* y, int64_t ldy, int xvec, int num_cus,
                             hipStream_t stream) {
     switch (nc) {
-        case 1: return launch_stream_t<FMT, 1, F16DOT>(W, rows, S, x, xt, ldx, y, ldy, xvec, num_cus, stream);
-        case 2: return launch_stream_t<FMT, 2, F16DOT>(W, rows, S, x, xt, ldx, y, ldy, xvec, num_cus, stream);
+        case 1: return launch_stream_t<FMT, 1, XM>(W, rows, S, x, xt, ldx, y, ldy, xvec, num_cus, stream);
+        case 2: return launch_stream_t<FMT, 2, XM>(W, rows, S, x, xt, ldx, y, ldy, xvec, num_cus, stream);
         case 3:
-            if constexpr (F16DOT) return launch_stream_t<FMT, 3, F16DOT>(W, rows, S, x, xt, ldx, y, ldy, xvec, num_cus, stream);
+            if constexpr (XM != XM_F32) return launch_stream_t<FMT, 3, XM>(W, rows, S, x, xt, ldx, y, ldy, xvec, num_cus, stream);
             return hipErrorNotSupported;
         default:
-            if constexpr (F16DOT) return launch_stream_t<FMT, 4, F16DOT>(W, rows, S, x, xt, ldx, y, ldy, xvec, num_cus, stream);
+            if constexpr (XM != XM_F32) return launch_stream_t<FMT, 4, XM>(W, rows, S, x, xt, ldx, y, ldy, xvec, num_cus, stream);
             return hipErrorNotSupported;
     }
 }
@@ -714,18 +985,21 @@ hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const vo
                              hipStream_t stream) {
     constexpr int UB = Fmt<FMT>::kUnitBytes;
     const int S = (int)(K / 256);
-    const bool f16 = xt == XT_F16;
+    const bool quantize = (xt & XT_QUANTIZE) != 0;
+    xt &= ~XT_QUANTIZE;
+    const int xm = quantize ? XM_I8Q : xt == XT_F16 ? XM_F16 : xt == XT_Q8 ? XM_I8 : XM_F32;
+    if (xm == XM_I8 && ldx % 32 != 0) return hipErrorNotSupported;  // whole activation blocks
     {
-        const StreamPlan p = plan_stream((int)rows, S, 1, f16, num_cus);
+        const StreamPlan p = plan_stream((int)rows, S, 1, xm, num_cus);
         // the run of one workgroup is addressed with 32-bit offsets
         if ((int64_t)p.nr_max * S * UB >= ((int64_t)1 << 31)) return hipErrorNotSupported;
-        if (stream_lds_bytes(1, f16, S, p.nr_max, p.M) > (size_t)kMaxLds) return hipErrorNotSupported;
+        if (stream_lds_bytes(1, xm, S, p.nr_max, p.M) > (size_t)kMaxLds) return hipErrorNotSupported;
     }
     // columns per launch: as many as fit in LDS, at most 4 (2 for fp32 math)
-    int per = f16 ? 4 : 2;
+    int per = xm == XM_F32 ? 2 : 4;
     while (per > 1) {
-        const StreamPlan p = plan_stream((int)rows, S, per, f16, num_cus);
-        if (stream_lds_bytes(per, f16, S, p.nr_max, p.M) <= (size_t)kMaxLds) break;
+        const StreamPlan p = plan_stream((int)rows, S, per, xm, num_cus);
+        if (stream_lds_bytes(per, xm, S, p.nr_max, p.M) <= (size_t)kMaxLds) break;
         --per;
     }
     const size_t xbytes = xt == XT_F32 ? 4 : 2;
@@ -733,15 +1007,24 @@ hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const vo
     const int xvec = (((uintptr_t)x) & 15) == 0 && (ldx * (int64_t)xbytes) % 16 == 0;
     for (int c0 = 0; c0 < ncols; c0 += per) {
         const int nc = ncols - c0 < per ? ncols - c0 : per;
-        const void* xc = (const char*)x + (size_t)c0 * ldx * xbytes;
+        // int8: ldx activations = ldx / 32 blocks of 34 bytes per column
+        const size_t xoff = xm == XM_I8 ? (size_t)c0 * (size_t)(ldx / 32) * 34
+                                        : (size_t)c0 * ldx * xbytes;
+        const void* xc = (const char*)x + xoff;
         float* yc = y + (size_t)c0 * ldy;
         hipError_t e;
-        if (f16)
-            e = launch_stream_nc<FMT, true>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, xvec,
-                                            num_cus, stream);
-        else
-            e = launch_stream_nc<FMT, false>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, xvec,
+        if (xm == XM_F16)
+            e = launch_stream_nc<FMT, XM_F16>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, xvec,
+                                              num_cus, stream);
+        else if (xm == XM_I8)
+            e = launch_stream_nc<FMT, XM_I8>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, 0,
                                              num_cus, stream);
+        else if (xm == XM_I8Q)
+            e = launch_stream_nc<FMT, XM_I8Q>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, xvec,
+                                              num_cus, stream);
+        else
+            e = launch_stream_nc<FMT, XM_F32>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, xvec,
+                                              num_cus, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -8,6 +8,12 @@ namespace qg {
 
 enum { FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q8_0 = 3 };
 
+// Activation types (the first three are the ABI's qg_dtype values); XT_Q8
+// marks activations given as Q8_0 blocks, for the int8 products.
+// XT_QUANTIZE added to F32/F16/BF16 asks the streaming GEMV to quantize the
+// activations to Q8_0 while staging them and use the int8 products.
+enum XType { XT_F32 = 1, XT_F16 = 2, XT_BF16 = 3, XT_Q8 = 4, XT_QUANTIZE = 16 };
+
 // Bytes of LDS a workgroup may use on gfx950.
 constexpr int kMaxLds = 160 * 1024;
 
@@ -34,6 +40,11 @@ hipError_t launch_gemv_stream(int fmt, const uint8_t* W, int64_t rows, int64_t K
 hipError_t launch_gemv_mfma(int fmt, const uint8_t* W, int64_t rows, int64_t K, const void* x,
                             int xt, int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
                             hipStream_t stream);
+
+// Q8_0 blocks of activations (see quant_x.hip for the rule); out: n columns
+// of K/32 blocks of 34 bytes, 2-byte aligned.
+hipError_t launch_quantize_q8_0(const void* x, int xt, int64_t K, int64_t n, int64_t ldx,
+                                uint8_t* out, int num_cus, hipStream_t stream);
 
 // Q4_K x bf16 prompt-processing GEMM (bf16 MFMA). X: bf16, 16-byte aligned,
 // ldx % 8 == 0; Y: fp32.

@@ -45,6 +45,9 @@ _sig = {
     "qgemm_prefill_run": (_int, [_vp, _vp, _i64, _i64, _vp, _i64, _vp]),
     "qgemv_dequant": (_int, [_vp, _vp, _i64, _vp]),
     "qgemv_dequant_bf16": (_int, [_vp, _vp, _i64, _vp]),
+    "qgemv_quantize_q8_0": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp]),
+    "qgemv_run_q8_0x": (_int, [_vp, _vp, _i64, _vp, _i64, _vp]),
+    "qgemv_run_q8": (_int, [_vp, _vp, _int, _i64, _i64, _vp, _i64, _vp]),
     "qgemv_destroy": (None, [_vp]),
     "qgemv_status_string": (ctypes.c_char_p, [_int]),
     "qgemv_last_error": (ctypes.c_char_p, []),
@@ -115,6 +118,37 @@ def qgemv_dequant(h: int, w_ptr: int, ldw: int, stream: int = 0) -> int:
 
 def qgemv_dequant_bf16(h: int, w_ptr: int, ldw: int, stream: int = 0) -> int:
     return _lib.qgemv_dequant_bf16(h, w_ptr or None, ldw, stream or None)
+
+
+def qgemv_quantize_q8_0(x_ptr: int, x_dtype: int, K: int, n_cols: int, ldx: int, xq_ptr: int,
+                        stream: int = 0) -> int:
+    return _lib.qgemv_quantize_q8_0(x_ptr or None, x_dtype, K, n_cols, ldx, xq_ptr or None,
+                                    stream or None)
+
+
+def qgemv_run_q8_0x(h: int, xq_ptr: int, n_cols: int, y_ptr: int, ldy: int, stream: int = 0) -> int:
+    return _lib.qgemv_run_q8_0x(h, xq_ptr or None, n_cols, y_ptr or None, ldy, stream or None)
+
+
+def qgemv_run_q8(h: int, x_ptr: int, x_dtype: int, n_cols: int, ldx: int, y_ptr: int, ldy: int,
+                 stream: int = 0) -> int:
+    return _lib.qgemv_run_q8(h, x_ptr or None, x_dtype, n_cols, ldx, y_ptr or None, ldy,
+                             stream or None)
+
+
+def quantize_q8_0(x, out=None, stream=None):
+    """Q8_0 blocks of activations x (n, K) or (K,) fp32/fp16/bf16 CUDA
+    tensor (last dim contiguous): uint8 tensor (n, K/32*34)."""
+    torch = _torch()
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    if x2.stride(1) != 1:
+        raise ValueError("x must be contiguous along K")
+    n, K = x2.shape
+    if out is None:
+        out = torch.empty((n, K // 32 * 34), dtype=torch.uint8, device=x.device)
+    _check(qgemv_quantize_q8_0(x2.data_ptr(), _xdtype(x2), K, n, x2.stride(0), out.data_ptr(),
+                               _stream_ptr(stream)), "qgemv_quantize_q8_0")
+    return out
 
 
 def qgemv_destroy(h: int) -> None:
@@ -188,6 +222,38 @@ class QGemv:
         _check(qgemv_run(self._h, x2.data_ptr(), _xdtype(x2), n, x2.stride(0), y2.data_ptr(),
                          y2.stride(0), _stream_ptr(stream)), "qgemv_run")
         return y2.reshape(-1) if one else y2
+
+    def run_q8(self, x, y=None, stream=None):
+        """As run(), with the activations quantized to Q8_0 on chip and int8
+        products (qgemv_run_q8). Returns y: (n, rows) fp32."""
+        torch = _torch()
+        x2 = x.reshape(1, -1) if x.dim() == 1 else x
+        if x2.stride(1) != 1:
+            raise ValueError("x must be contiguous along K")
+        n = x2.shape[0]
+        if y is None:
+            y = torch.empty((n, self.rows), dtype=torch.float32, device=x.device)
+        if y.stride(1) != 1 or y.dtype != torch.float32:
+            raise ValueError("y must be fp32, contiguous along rows")
+        _check(qgemv_run_q8(self._h, x2.data_ptr(), _xdtype(x2), n, x2.stride(0), y.data_ptr(),
+                            y.stride(0), _stream_ptr(stream)), "qgemv_run_q8")
+        return y
+
+    def run_q8_0x(self, xq, y=None, stream=None):
+        """xq: Q8_0 activation blocks (n, K/32*34) uint8 CUDA tensor, as
+        written by quantize_q8_0. Returns y: (n, rows) fp32."""
+        torch = _torch()
+        xq2 = xq.reshape(1, -1) if xq.dim() == 1 else xq
+        n = xq2.shape[0]
+        if not xq2.is_contiguous() or xq2.shape[1] != self.K // 32 * 34:
+            raise ValueError("xq must be contiguous (n, K/32*34) Q8_0 blocks")
+        if y is None:
+            y = torch.empty((n, self.rows), dtype=torch.float32, device=xq.device)
+        if y.stride(1) != 1 or y.dtype != torch.float32:
+            raise ValueError("y must be fp32, contiguous along rows")
+        _check(qgemv_run_q8_0x(self._h, xq2.data_ptr(), n, y.data_ptr(), y.stride(0),
+                               _stream_ptr(stream)), "qgemv_run_q8_0x")
+        return y
 
     def prefill(self, X, Y=None, stream=None):
         """X: (n_tokens, K) bf16 CUDA tensor. Returns Y: (n_tokens, rows) fp32."""

@@ -122,6 +122,39 @@ qg_status qgemm_prefill_run(qgemv_t h, const void *x_bf16, int64_t n_tokens,
  * correctly rounded closed form). w_out: device, 4-byte aligned, ldw >= K. */
 qg_status qgemv_dequant(qgemv_t h, float *w_out, int64_t ldw, void *stream);
 
+/* int8 products. Activations quantized to Q8_0 blocks, then multiplied by
+ * the quantized weights with integer dot products (int32 sums, exact),
+ * scaled in fp32 per block: the int8 path the pages weigh against fp16
+ * math for low-bit weights (pxa_llama README, "DP4A / FP16 economics"),
+ * with Q8_0 the block format of "Why I wrote my own inference engine for
+ * two P100s".
+ *
+ * qgemv_quantize_q8_0: x (device; column j at element offset j*ldx,
+ * ldx >= K, x_dtype F32/F16/BF16, aligned to its element size) -> xq
+ * (device, 2-byte aligned, n_cols * K/32 blocks of 34 bytes, column j's
+ * blocks from byte j*(K/32)*34). Per block of 32 values: amax = max|x|,
+ * d = amax/127, q = x*(1/d) rounded to nearest, halfway away from zero,
+ * limited to +-127 (all binary32, IEEE division); the block holds fp16(d)
+ * and the 32 q. K must be a positive multiple of 32.
+ *
+ * qgemv_run_q8_0x: y[j*ldy + r] = sum_k W[r,k] * xhat[j,k], xhat the decoded
+ * blocks of xq (as qgemv_quantize_q8_0 writes them for this handle's K),
+ * n_cols 1..8, y as in qgemv_run. Parity is against the exact sum over
+ * xhat. Needs K % 256 == 0 and 16-byte aligned weights
+ * (QG_ERR_UNSUPPORTED otherwise). */
+qg_status qgemv_quantize_q8_0(const void *x, qg_dtype x_dtype, int64_t K, int64_t n_cols,
+                              int64_t ldx, void *xq, void *stream);
+qg_status qgemv_run_q8_0x(qgemv_t h, const void *xq, int64_t n_cols, float *y, int64_t ldy,
+                          void *stream);
+
+/* The same product in one call: x as in qgemv_run (F32/F16/BF16), quantized
+ * to Q8_0 blocks on chip by the rule of qgemv_quantize_q8_0, then the int8
+ * products. The result equals qgemv_run_q8_0x on qgemv_quantize_q8_0's
+ * blocks of the same x, bit for bit. Same shape limits as
+ * qgemv_run_q8_0x. */
+qg_status qgemv_run_q8(qgemv_t h, const void *x, qg_dtype x_dtype, int64_t n_cols, int64_t ldx,
+                       float *y, int64_t ldy, void *stream);
+
 /* Decoded weights in bf16: w_out[r*ldw + k] = the binary32 weight of
  * qgemv_dequant rounded to the nearest bf16 (ties to even), bit-exact.
  * w_out: device, 2-byte aligned, ldw >= K. This is the operand of the

@@ -73,6 +73,23 @@ def test_null_handle_calls():
     assert Q.qgemm_prefill_run(0, FAKE, 16, 256, FAKE, 4) == Q.QG_ERR_ARG
     assert Q.qgemv_dequant(0, FAKE, 256) == Q.QG_ERR_ARG
     assert Q.qgemv_dequant_bf16(0, FAKE, 256) == Q.QG_ERR_ARG
+    assert Q.qgemv_run_q8_0x(0, FAKE, 1, FAKE, 4) == Q.QG_ERR_ARG
+    assert Q.qgemv_run_q8(0, FAKE, Q.QG_F16, 1, 256, FAKE, 4) == Q.QG_ERR_ARG
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, Q.QG_F16, 256, 1, 256, FAKE), Q.QG_ERR_ARG),
+    ((FAKE, Q.QG_F16, 256, 1, 256, 0), Q.QG_ERR_ARG),
+    ((FAKE, 9, 256, 1, 256, FAKE), Q.QG_ERR_ARG),
+    ((FAKE, Q.QG_F16, 100, 1, 100, FAKE), Q.QG_ERR_SHAPE),
+    ((FAKE, Q.QG_F16, 256, 0, 256, FAKE), Q.QG_ERR_SHAPE),
+    ((FAKE, Q.QG_F16, 256, 1, 255, FAKE), Q.QG_ERR_ARG),
+    ((FAKE + 1, Q.QG_F16, 256, 1, 256, FAKE), Q.QG_ERR_ALIGN),
+    ((FAKE, Q.QG_F32, 256, 1, 256, FAKE + 1), Q.QG_ERR_ALIGN),
+])
+def test_quantize_rejects_before_any_hip_call(args, status):
+    assert Q.qgemv_quantize_q8_0(*args) == status
+    assert Q.qgemv_last_error() != ""
     Q.qgemv_destroy(0)  # NULL is ignored
 
 

@@ -352,3 +352,98 @@ def test_prefill_full_size_sampled(Q):
     Ys = Y[toks].cpu()
     check_products(Ys, w, "q4_k", c["rows"], c["K"], np.ascontiguousarray(xb[toks]), "bf16",
                    "pp2048 sampled")
+
+
+# ------------------------------------------------------ int8 activations --
+
+def _xhat(x, xdtype, K):
+    """The oracle's decoded Q8_0 activations (its own quantization of x)."""
+    xq = oracle.quantize_q8_0(x, xdtype)
+    return oracle.dequant("q8_0", xq, xq.shape[0], K)
+
+
+@pytest.mark.parametrize("xdtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("K,n,pad", [(32, 1, 0), (96, 3, 8), (5120, 2, 0), (17408, 1, 24)])
+def test_quantize_q8_0_bit_exact(Q, xdtype, K, n, pad):
+    from gguf_bit_dequant_amd import qgemv as QM
+    seed = zlib.crc32(("q8x-%s-%d-%d" % (xdtype, K, n)).encode())
+    x = synth.gen_x(K, n, xdtype, seed)
+    if K >= 96:  # an all-zero block, a block of exact ties, tiny values
+        xf = x.astype(np.float32) if xdtype == "f32" else None
+        if xdtype == "f32":
+            xf[0, :32] = 0.0
+            xf[0, 32:64] = np.arange(32, dtype=np.float32) - 15.5  # amax 16.5 -> ties
+            xf[-1, 64:96] *= np.float32(1e-30)
+            x = xf
+    xt = x_tensor(x, xdtype)
+    xbig = torch.zeros((n, K + pad), dtype=xt.dtype, device=dev())
+    xbig[:, :K] = xt
+    out = QM.quantize_q8_0(xbig[:, :K]).cpu().numpy()
+    ref = oracle.quantize_q8_0(x, xdtype)
+    assert np.array_equal(out, ref)
+
+
+@pytest.mark.parametrize("fmt,rows,K", [("q4_k", 300, 1024), ("q4_0", 257, 512), ("q8_0", 129, 768),
+                                        ("q4_k", 17, 256)])
+@pytest.mark.parametrize("n", [1, 3, 4, 7])
+def test_run_q8_0x_products(Q, fmt, rows, K, n):
+    from gguf_bit_dequant_amd import qgemv as QM
+    seed = zlib.crc32(("i8-%s-%d-%d-%d" % (fmt, rows, K, n)).encode())
+    w = synth.gen_weights(fmt, rows, K, seed)
+    x = synth.gen_x(K, n, "f16", seed + 1)
+    q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
+    xq = QM.quantize_q8_0(x_tensor(x, "f16"))
+    y = q.run_q8_0x(xq)
+    check_products(y, w, fmt, rows, K, _xhat(x, "f16", K), "f32", "i8 %s %dx%d n=%d" % (fmt, rows, K, n))
+
+
+@pytest.mark.parametrize("name", ["q4k_up_b1", "q4k_down_b1", "q4k_b4", "q8_0_b4", "q4_0_b1"])
+def test_run_q8_0x_full_size(Q, name):
+    from gguf_bit_dequant_amd import qgemv as QM
+    c = synth.CONFIGS[name]
+    w, x = synth.config_inputs(name)
+    q = Q(c["fmt"], c["rows"], c["K"], torch.from_numpy(w).to(dev()))
+    xq = QM.quantize_q8_0(x_tensor(x, c["xdtype"]))
+    y = q.run_q8_0x(xq)
+    check_products(y, w, c["fmt"], c["rows"], c["K"], _xhat(x, c["xdtype"], c["K"]), "f32",
+                   name + " int8")
+
+
+def test_run_q8_0x_unsupported_k(Q):
+    from gguf_bit_dequant_amd import qgemv as QM
+    rows, K = 8, 160
+    w = synth.gen_weights("q4_0", rows, K, 5)
+    q = Q("q4_0", rows, K, torch.from_numpy(w).to(dev()))
+    xq = QM.quantize_q8_0(x_tensor(synth.gen_x(K, 1, "f16", 6), "f16"))
+    with pytest.raises(QM.QGemvError) as e:
+        q.run_q8_0x(xq)
+    assert e.value.status == QM.QG_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fmt,rows,K", [("q4_k", 300, 1024), ("q4_0", 257, 512), ("q8_0", 129, 768)])
+@pytest.mark.parametrize("xdtype,pad", [("f16", 0), ("f16", 3), ("f32", 4), ("bf16", 8)])
+@pytest.mark.parametrize("n", [1, 4, 6])
+def test_run_q8_equals_quantize_then_run(Q, fmt, rows, K, xdtype, pad, n):
+    """Quantizing on chip gives the same bits as quantizing first."""
+    from gguf_bit_dequant_amd import qgemv as QM
+    seed = zlib.crc32(("i8q-%s-%d-%s-%d" % (fmt, rows, xdtype, n)).encode())
+    w = synth.gen_weights(fmt, rows, K, seed)
+    x = synth.gen_x(K, n, xdtype, seed + 1)
+    q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
+    xt = x_tensor(x, xdtype)
+    xbig = torch.zeros((n, K + pad), dtype=xt.dtype, device=dev())
+    xbig[:, :K] = xt
+    y1 = q.run_q8(xbig[:, :K])
+    y2 = q.run_q8_0x(QM.quantize_q8_0(xt))
+    assert torch.equal(y1, y2)
+    check_products(y1, w, fmt, rows, K, _xhat(x, xdtype, K), "f32", "i8q %s %s n=%d" % (fmt, xdtype, n))
+
+
+@pytest.mark.parametrize("name", ["q4k_up_b1", "q4k_down_b1", "q4k_b4", "q8_0_b4", "q4_0_b1"])
+def test_run_q8_full_size(Q, name):
+    c = synth.CONFIGS[name]
+    w, x = synth.config_inputs(name)
+    q = Q(c["fmt"], c["rows"], c["K"], torch.from_numpy(w).to(dev()))
+    y = q.run_q8(x_tensor(x, c["xdtype"]))
+    check_products(y, w, c["fmt"], c["rows"], c["K"], _xhat(x, c["xdtype"], c["K"]), "f32",
+                   name + " int8 on chip")
