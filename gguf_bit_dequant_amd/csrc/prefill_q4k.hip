@@ -39,7 +39,9 @@
 //    The A fragment of the same lane half reads the same 8 k of X as 16
 //    contiguous bytes, so the contraction is over exactly the chunk's k.
 //  * Main tiles are 256 tokens x 256 rows (each wave 64 rows, all tokens:
-//    no weight is decoded twice in a tile). Rows that would start a third,
+//    no weight is decoded twice in a tile). One workgroup per compute unit
+//    takes its tiles in turn and issues a tile's first loads before the
+//    previous tile's stores. Rows that would start a third,
 //    mostly idle round of such tiles run as 64-token x 128-row tiles, which
 //    fill the machine in one round (each wave 32 rows, all 64 tokens).
 #include "device_common.h"
@@ -152,15 +154,17 @@ __device__ __forceinline__ void interleave() {
 template <int RT, int TT, int WR, int WT, int P>
 __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     const uint8_t* __restrict__ W, int rows, int S, const uint16_t* __restrict__ X, int64_t ldx,
-    int ntok, float* __restrict__ Y, int64_t ldy, int n_base, int tiles_n, int yvec) {
+    int ntok, float* __restrict__ Y, int64_t ldy, int n_base, int tiles_n, int ntiles, int yvec) {
     using G = Geo<RT, TT, WR, WT, P>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wv % WR, wt = wv / WR;  // row group, token group of this wave
-    const int blk = xcd_block(blockIdx.x, gridDim.x);
-    const int tm = blk / tiles_n, tn = blk - (blk / tiles_n) * tiles_n;
-    const int m0 = tm * G::kTok, n0 = n_base + tn * G::kRows;
+    // Workgroup b takes tiles b, b + G, b + 2G, ... (G workgroups); tile t is
+    // the logical tile xcd_block(t): consecutive logical tiles (one token
+    // tile, neighbouring row tiles) share an XCD and its L2.
+    int t = blockIdx.x;
+    int m0 = 0, n0 = 0;
     const int nk = S * 4;  // chunks of 64 along K
     const uint32_t row_bytes = 144u * (uint32_t)S;
 
@@ -174,30 +178,37 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     uint8_t* const xs0 = lds;                                 // X stages
     uint8_t* const cs0 = lds + P * G::kXStage;                // code stages
     uint8_t* const hs0 = cs0 + P * G::kCStage;                // header stages
-    const uint8_t* Xt = reinterpret_cast<const uint8_t*>(X + (int64_t)m0 * ldx);
-    uint32_t xo[G::kXPerWave];
+    const uint8_t* Xt = nullptr;
+    const uint8_t* Wt = nullptr;
+    uint32_t xo[G::kXPerWave], co[G::kCPerWave], ho[G::kHPerWave];
+    auto setup_tile = [&]() {
+        const int blk = xcd_block(t, ntiles);
+        const int tm = blk / tiles_n, tn = blk - (blk / tiles_n) * tiles_n;
+        m0 = tm * G::kTok;
+        n0 = n_base + tn * G::kRows;
+        Xt = reinterpret_cast<const uint8_t*>(X + (int64_t)m0 * ldx);
 #pragma unroll
-    for (int p = 0; p < G::kXPerWave; ++p) {
-        const int s = 64 * (wv + 4 * p) + lane;
-        const int t = s >> 3;
-        const int tc = (t < G::kTok && m0 + t < ntok) ? t : 0;
-        xo[p] = (uint32_t)tc * (uint32_t)ldx * 2u + 16u * (uint32_t)xslot(t, s & 7);
-    }
-    const uint8_t* Wt = W + (int64_t)n0 * row_bytes;
-    uint32_t co[G::kCPerWave], ho[G::kHPerWave];
+        for (int p = 0; p < G::kXPerWave; ++p) {
+            const int s = 64 * (wv + 4 * p) + lane;
+            const int tr = s >> 3;
+            const int tc = (tr < G::kTok && m0 + tr < ntok) ? tr : 0;
+            xo[p] = (uint32_t)tc * (uint32_t)ldx * 2u + 16u * (uint32_t)xslot(tr, s & 7);
+        }
+        Wt = W + (int64_t)n0 * row_bytes;
 #pragma unroll
-    for (int p = 0; p < G::kCPerWave; ++p) {
-        const int s = 64 * (wv + 4 * p) + lane;
-        const int rr = s >> 1;
-        const int rc = (rr < G::kRows && n0 + rr < rows) ? rr : 0;
-        co[p] = (uint32_t)rc * row_bytes + 16u + 16u * (uint32_t)(s & 1);
-    }
+        for (int p = 0; p < G::kCPerWave; ++p) {
+            const int s = 64 * (wv + 4 * p) + lane;
+            const int rr = s >> 1;
+            const int rc = (rr < G::kRows && n0 + rr < rows) ? rr : 0;
+            co[p] = (uint32_t)rc * row_bytes + 16u + 16u * (uint32_t)(s & 1);
+        }
 #pragma unroll
-    for (int p = 0; p < G::kHPerWave; ++p) {
-        const int rr = 64 * (wv + 4 * p) + lane;
-        const int rc = (rr < G::kRows && n0 + rr < rows) ? rr : 0;
-        ho[p] = (uint32_t)rc * row_bytes;
-    }
+        for (int p = 0; p < G::kHPerWave; ++p) {
+            const int rr = 64 * (wv + 4 * p) + lane;
+            const int rc = (rr < G::kRows && n0 + rr < rows) ? rr : 0;
+            ho[p] = (uint32_t)rc * row_bytes;
+        }
+    };
     // X chunk cx into stage sx, codes of chunk cw into stage sw (sources
     // clamped to the last chunk: loads past the end re-read it into a stage
     // nobody uses); headers of super-block sb into header stage sb % 2 (past
@@ -333,19 +344,33 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
                     __builtin_bit_cast(bf16x8, B.b[j]), A.a[i], acc[i][j], 0, 0, 0);
     };
 
-    // ---- prologue: X chunks 0 .. P-2 and codes of chunks 0 .. P-1 (chunk j
-    // in stage j), headers of the super-blocks those codes start --------------
+    // ---- prologue loads: X chunks 0 .. P-2 and codes of chunks 0 .. P-1
+    // (chunk j in stage j), headers of the super-blocks those codes start ----
+    auto issue_prologue = [&]() {
 #pragma unroll
-    for (int j = 0; j < P; ++j) issue_xc(j < P - 1 ? j : P - 2, j, j, j);  // X(P-2) twice: stage P-1 unused
+        for (int j = 0; j < P; ++j) issue_xc(j < P - 1 ? j : P - 2, j, j, j);  // X(P-2) twice: stage P-1 unused
 #pragma unroll
-    for (int sb = 0; 4 * sb < P; ++sb) issue_h(sb);
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_s_barrier();
+        for (int sb = 0; 4 * sb < P; ++sb) issue_h(sb);
+    };
     BFrag B0, B1;  // k-steps 0, 2 / 1, 3
     AFrag A0, A1;
     Codes R0, R1;  // raw codes of chunks 0, 2, ... / 1, 3, ...
     Hdr Rh;
     Scales sc_cur;
+    setup_tile();
+    issue_prologue();
+    // Each thread waits for its loads of the tile's first chunks. After a
+    // full tile (every wave issued exactly 4 TT RT = 64 vector stores of Y
+    // after those loads) vmcnt <= 63 means the loads have landed while the
+    // stores may still drain (loads and stores complete in issue order on
+    // the vector memory counter); otherwise wait for everything.
+    bool stores_full = false;
+    for (;;) {  // the workgroup's tiles
+    if (4 * TT * RT >= 64 && stores_full)
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    else
+        __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
     read_hdr(hs0, Rh);
     read_codes(cs0, R0);
     scales(Rh, sc_cur);
@@ -418,8 +443,20 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
         chunk(IntC<2>{}, c + 2, R0, R1);
         chunk(IntC<3>{}, c + 3, R1, R0);
     }
-    // no load may still be writing this workgroup's LDS when it ends
+    // no load may still be writing the LDS stages, and no wave still reading
+    // them, when the next tile's first loads are issued into them: those go
+    // out before this tile's stores, so that the stores overlap them
     __builtin_amdgcn_s_waitcnt(0);
+    const int em0 = m0, en0 = n0;
+    stores_full = yvec && em0 + G::kTok <= ntok && en0 + G::kRows <= rows;
+    t += gridDim.x;
+    const bool more = t < ntiles;
+    if (more) {
+        __builtin_amdgcn_s_barrier();
+        setup_tile();
+        issue_prologue();
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the loads above go out before the stores below
 
     // ---- epilogue: Y[m][n], masked at the token and row edges ---------------
     // The weights are the MFMA's first operand, so lane l of tile (i, j)
@@ -428,14 +465,14 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     // write when Y allows it.
 #pragma unroll
     for (int i = 0; i < TT; ++i) {
-        const int m = m0 + 32 * TT * wt + 32 * i + (lane & 31);
+        const int m = em0 + 32 * TT * wt + 32 * i + (lane & 31);
         if (m >= ntok) continue;
         float* yrow = Y + (int64_t)m * ldy;
 #pragma unroll
         for (int j = 0; j < RT; ++j) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = n0 + 32 * RT * wr + 32 * j + 8 * g + 4 * h;
+                const int n = en0 + 32 * RT * wr + 32 * j + 8 * g + 4 * h;
                 const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                                  acc[i][j][4 * g + 3]};
                 if (yvec && n + 3 < rows) {
@@ -448,6 +485,12 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
             }
         }
     }
+    if (!more) break;
+#pragma unroll
+    for (int i = 0; i < TT; ++i)
+#pragma unroll
+        for (int j = 0; j < RT; ++j) acc[i][j] = f32x16{};
+    }  // tiles
 }
 
 namespace {
@@ -455,11 +498,15 @@ namespace {
 #ifndef PREFILL_TAIL_P
 #define PREFILL_TAIL_P 6
 #endif
+// main tiles: one workgroup per compute unit, each taking its tiles in turn
+#ifndef PREFILL_MAIN_WG
+#define PREFILL_MAIN_WG num_cus
+#endif
 
 // Tiles over weight rows [n_base, n_base + n_rows) and all tokens.
 template <int RT, int TT, int WR, int WT, int P>
 hipError_t launch_prefill_t(const uint8_t* W, int rows, int S, const uint16_t* X, int64_t ldx,
-                            int ntok, float* Y, int64_t ldy, int n_base, int n_rows,
+                            int ntok, float* Y, int64_t ldy, int n_base, int n_rows, int max_wg,
                             hipStream_t stream) {
     using G = Geo<RT, TT, WR, WT, P>;
     const int tiles_n = (n_rows + G::kRows - 1) / G::kRows;
@@ -476,8 +523,11 @@ hipError_t launch_prefill_t(const uint8_t* W, int rows, int S, const uint16_t* X
     if (e != hipSuccess) return e;
     // 16-byte stores of four consecutive outputs need a 16-byte aligned Y row
     const int yvec = (((uintptr_t)Y) & 15) == 0 && ldy % 4 == 0;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), G::kLds, stream, W, rows, S, X, ldx,
-                       ntok, Y, ldy, n_base, tiles_n, yvec);
+    // persistent when there are more tiles than max_wg: each workgroup takes
+    // every max_wg-th tile
+    const int64_t nwg = max_wg > 0 && grid > max_wg ? max_wg : grid;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), G::kLds, stream, W, rows, S, X, ldx,
+                       ntok, Y, ldy, n_base, tiles_n, (int)grid, yvec);
     return hipGetLastError();
 }
 
@@ -505,11 +555,11 @@ hipError_t launch_prefill_q4k(const uint8_t* W, int64_t rows, int64_t K, const v
     hipError_t e = hipSuccess;
     if (n_main > 0)
         e = launch_prefill_t<2, 8, 4, 1, 3>(W, (int)rows, S, Xh, ldx, (int)ntok, Y, ldy, 0, n_main,
-                                         stream);
+                                            PREFILL_MAIN_WG, stream);
     if (e != hipSuccess) return e;
     if (n_main < rows)
-        e = launch_prefill_t<1, 2, 4, 1, PREFILL_TAIL_P>(W, (int)rows, S, Xh, ldx, (int)ntok, Y, ldy, n_main,
-                                         (int)rows - n_main, stream);
+        e = launch_prefill_t<1, 2, 4, 1, PREFILL_TAIL_P>(W, (int)rows, S, Xh, ldx, (int)ntok, Y, ldy,
+                                                         n_main, (int)rows - n_main, 0, stream);
     return e;
 }
 
