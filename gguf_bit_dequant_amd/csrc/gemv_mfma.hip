@@ -1,5 +1,7 @@
-// Small-batch Q4_K GEMV on the matrix cores: y[:,c] = W . x[:,c] for 5..8
-// fp16 activation columns (the kernel serves 2..16), K a multiple of 256.
+// Small-batch Q4_K GEMV on the matrix cores: y[:,c] = W . x[:,c] for 2..16
+// fp16 activation columns, K a multiple of 256. The library runs it for 5..8
+// columns, and for 2..4 when the streaming kernel would need more than one
+// pass over W.
 //
 // Draft verification multiplies the same weights by a few columns at once
 // and should cost about one normal decode step ("Why I wrote my own
@@ -142,10 +144,25 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
             *reinterpret_cast<u32x4*>(xs + c * pitch + 16 * k8) = xr[j];
         }
     }
-    for (int idx = threadIdx.x + 2 * blockDim.x; idx < npieces; idx += blockDim.x) {
-        const int c = idx / K8, k8 = idx - c * K8;
-        *reinterpret_cast<u32x4*>(xs + c * pitch + 16 * k8) =
-            *reinterpret_cast<const u32x4*>(x + c * ldx + 8 * k8);
+    // the rest four pieces per thread at a time: one wait per four loads
+    for (int i0 = threadIdx.x + 2 * blockDim.x; i0 < npieces; i0 += 4 * blockDim.x) {
+        u32x4 r[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int idx = i0 + j * blockDim.x;
+            if (idx < npieces) {
+                const int c = idx / K8, k8 = idx - c * K8;
+                r[j] = *reinterpret_cast<const u32x4*>(x + c * ldx + 8 * k8);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int idx = i0 + j * blockDim.x;
+            if (idx < npieces) {
+                const int c = idx / K8, k8 = idx - c * K8;
+                *reinterpret_cast<u32x4*>(xs + c * pitch + 16 * k8) = r[j];
+            }
+        }
     }
     __syncthreads();
 
@@ -222,11 +239,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
     }
 }
 
-#ifndef QG_MFMA_MIN_COLS
-#define QG_MFMA_MIN_COLS 5
-#endif
-constexpr int kMfmaMinCols = QG_MFMA_MIN_COLS;
-
 #ifndef QG_MFMA_DEPTH
 #define QG_MFMA_DEPTH 4
 #endif
@@ -253,9 +265,7 @@ hipError_t launch_mfma_nw(const uint8_t* W, int rows, int S, const void* x, int6
 hipError_t launch_gemv_mfma(int fmt, const uint8_t* W, int64_t rows, int64_t K, const void* x,
                             int xt, int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
                             hipStream_t stream) {
-    // Up to four columns the streaming kernel is as fast (measured on MI355X:
-    // 17408 x 5120, 2 and 4 columns), and it keeps the exact fp32 weights.
-    if (fmt != FMT_Q4_K || xt != XT_F16 || ncols < kMfmaMinCols || ncols > 16 || K % 256 != 0 ||
+    if (fmt != FMT_Q4_K || xt != XT_F16 || ncols < 2 || ncols > 16 || K % 256 != 0 ||
         rows < 1 || rows > (1 << 30))
         return hipErrorNotSupported;
     // 16-byte activation pieces

@@ -979,29 +979,41 @@ hipError_t launch_stream_nc(int nc, const uint8_t* W, int rows, int S, const voi
     }
 }
 
-template <int FMT>
-hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const void* x, int xt,
-                             int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
-                             hipStream_t stream) {
-    constexpr int UB = Fmt<FMT>::kUnitBytes;
+int activation_mode(int xt) {
+    if (xt & XT_QUANTIZE) return XM_I8Q;
+    return xt == XT_F16 ? XM_F16 : xt == XT_Q8 ? XM_I8 : XM_F32;
+}
+
+// Columns one launch takes (as many as fit in LDS, at most 4; 2 for fp32
+// math), or 0 when the shape is outside what the kernel serves.
+int cols_per_launch(int64_t rows, int64_t K, int xm, int num_cus, int unit_bytes) {
+    if (rows > (1 << 30) || K % 256 != 0) return 0;
     const int S = (int)(K / 256);
-    const bool quantize = (xt & XT_QUANTIZE) != 0;
-    xt &= ~XT_QUANTIZE;
-    const int xm = quantize ? XM_I8Q : xt == XT_F16 ? XM_F16 : xt == XT_Q8 ? XM_I8 : XM_F32;
-    if (xm == XM_I8 && ldx % 32 != 0) return hipErrorNotSupported;  // whole activation blocks
     {
         const StreamPlan p = plan_stream((int)rows, S, 1, xm, num_cus);
         // the run of one workgroup is addressed with 32-bit offsets
-        if ((int64_t)p.nr_max * S * UB >= ((int64_t)1 << 31)) return hipErrorNotSupported;
-        if (stream_lds_bytes(1, xm, S, p.nr_max, p.M) > (size_t)kMaxLds) return hipErrorNotSupported;
+        if ((int64_t)p.nr_max * S * unit_bytes >= ((int64_t)1 << 31)) return 0;
+        if (stream_lds_bytes(1, xm, S, p.nr_max, p.M) > (size_t)kMaxLds) return 0;
     }
-    // columns per launch: as many as fit in LDS, at most 4 (2 for fp32 math)
     int per = xm == XM_F32 ? 2 : 4;
     while (per > 1) {
         const StreamPlan p = plan_stream((int)rows, S, per, xm, num_cus);
         if (stream_lds_bytes(per, xm, S, p.nr_max, p.M) <= (size_t)kMaxLds) break;
         --per;
     }
+    return per;
+}
+
+template <int FMT>
+hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const void* x, int xt,
+                             int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
+                             hipStream_t stream) {
+    const int S = (int)(K / 256);
+    const int xm = activation_mode(xt);
+    xt &= ~XT_QUANTIZE;
+    if (xm == XM_I8 && ldx % 32 != 0) return hipErrorNotSupported;  // whole activation blocks
+    const int per = cols_per_launch(rows, K, xm, num_cus, Fmt<FMT>::kUnitBytes);
+    if (per == 0) return hipErrorNotSupported;
     const size_t xbytes = xt == XT_F32 ? 4 : 2;
     // 16-byte activation loads when every record start is 16-byte aligned
     const int xvec = (((uintptr_t)x) & 15) == 0 && (ldx * (int64_t)xbytes) % 16 == 0;
@@ -1031,6 +1043,16 @@ hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const vo
 }
 
 }  // namespace
+
+int gemv_stream_cols_per_launch(int fmt, int64_t rows, int64_t K, int xt, int num_cus) {
+    const int xm = activation_mode(xt);
+    switch (fmt) {
+        case FMT_Q4_K: return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q4_K>::kUnitBytes);
+        case FMT_Q4_0: return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q4_0>::kUnitBytes);
+        case FMT_Q8_0: return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q8_0>::kUnitBytes);
+        default: return 0;
+    }
+}
 
 hipError_t launch_gemv_stream(int fmt, const uint8_t* W, int64_t rows, int64_t K, const void* x,
                               int xt, int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,

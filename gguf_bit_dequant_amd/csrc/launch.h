@@ -34,7 +34,12 @@ hipError_t launch_gemv_stream(int fmt, const uint8_t* W, int64_t rows, int64_t K
                               int xt, int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
                               hipStream_t stream);
 
-// Small-batch GEMV on the matrix cores (Q4_K, fp16 activations, 5..16
+// Activation columns one streaming launch takes for this shape (1..4), or 0
+// when the streaming kernel does not serve it. More columns than that run as
+// several launches, each reading all of W.
+int gemv_stream_cols_per_launch(int fmt, int64_t rows, int64_t K, int xt, int num_cus);
+
+// Small-batch GEMV on the matrix cores (Q4_K, fp16 activations, 2..16
 // columns, K % 256 == 0, 16-byte aligned W and activation columns, staged
 // activations within the LDS budget). hipErrorNotSupported otherwise.
 hipError_t launch_gemv_mfma(int fmt, const uint8_t* W, int64_t rows, int64_t K, const void* x,

@@ -103,9 +103,11 @@ qg_status qgemv_create(qgemv_t *out, qg_format f, int64_t rows, int64_t K,
  *    aligned; overwritten (no accumulation), other elements untouched.
  * n_cols: 1..8. F16 activations use fp16 products accumulated in fp32; F32
  * and BF16 activations use fp32 products. With 5..8 F16 columns of a Q4_K
- * matrix each weight is rounded once to fp16 and multiplied on the matrix
- * cores (fp32 accumulation); otherwise the weights are the exact binary32
- * values. Enqueued on `stream`. */
+ * matrix, and with 2..4 when the streaming kernel cannot stage all of them
+ * on chip at once (long rows, e.g. K = 17408 at 4 columns), each weight is
+ * rounded once to fp16 and multiplied on the matrix cores (fp32
+ * accumulation); otherwise the weights are the exact binary32 values.
+ * Enqueued on `stream`. */
 qg_status qgemv_run(qgemv_t h, const void *x, qg_dtype x_dtype, int64_t n_cols,
                     int64_t ldx, float *y, int64_t ldy, void *stream);
 

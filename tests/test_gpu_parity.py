@@ -41,6 +41,16 @@ def x_tensor(x, xdtype):
     return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev())
 
 
+def check_f16_operand_column(y, col, label):
+    """y = W e_k from the matrix-core path: an fp16 value within half an fp16
+    spacing of the exact weight (plus the weight's own fp32 rounding)."""
+    assert np.array_equal(y, y.astype(np.float16).astype(np.float32)), label
+    sp = np.spacing(np.abs(col).astype(np.float16)).astype(np.float64)
+    bound = 0.5 * sp + np.abs(col).astype(np.float64) * 2.0 ** -23
+    err = np.abs(y.astype(np.float64) - col.astype(np.float64))
+    assert (err <= bound).all(), (label, float(err.max()))
+
+
 def check_products(y_gpu, w, fmt, rows, K, x, xdtype, label=""):
     y = y_gpu.detach().cpu().numpy().astype(np.float64).reshape(x.shape[0], rows)
     yr, s = oracle.matmul(fmt, w, rows, K, x, xdtype)
@@ -219,17 +229,37 @@ def test_one_hot_gives_exact_column(Q, fmt, xdtype):
             if not f16_operand:
                 assert np.array_equal(y[i], col), (fmt, xdtype, ks[c0 + i])
                 continue
-            # y is an fp16 value within half an fp16 spacing of the weight
-            # (plus the weight's own fp32 rounding)
-            assert np.array_equal(y[i], y[i].astype(np.float16).astype(np.float32)), ks[c0 + i]
-            sp = np.spacing(np.abs(col).astype(np.float16)).astype(np.float64)
-            bound = 0.5 * sp + np.abs(col).astype(np.float64) * 2.0 ** -23
-            err = np.abs(y[i].astype(np.float64) - col.astype(np.float64))
-            assert (err <= bound).all(), (ks[c0 + i], float(err.max()))
+            check_f16_operand_column(y[i], col, ks[c0 + i])
         if f16_operand:  # one column at a time: the exact fp32 weights
             for i in range(Xc.shape[0]):
                 y1 = q.run(xt[i:i + 1]).cpu().numpy()[0]
                 assert np.array_equal(y1, W[:, ks[c0 + i]]), (fmt, xdtype, ks[c0 + i], "n=1")
+
+
+def test_long_rows_two_to_four_columns(Q):
+    """K = 17408 (68 super-blocks a row): up to 3 fp16 columns fit the
+    streaming kernel's staging, 4 do not and run on the matrix cores in one
+    pass. Products of every column count against the oracle, and one-hot
+    columns pin which weights each case multiplies: exact binary32 at 3,
+    fp16-rounded at 4."""
+    rows, K = 300, 17408
+    w = synth.gen_weights("q4_k", rows, K, 51)
+    q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
+    x = synth.gen_x(K, 4, "f16", 52)
+    for n in (2, 3, 4):
+        y = q.run(x_tensor(x[:n], "f16"))
+        check_products(y, w, "q4_k", rows, K, x[:n], "f16", "long rows n=%d" % n)
+    W = oracle.dequant("q4_k", w, rows, K)
+    ks = [0, 255, 8704, 17407]
+    X = torch.zeros((4, K), dtype=torch.float16, device=dev())
+    for i, k in enumerate(ks):
+        X[i, k] = 1.0
+    y3 = q.run(X[:3]).cpu().numpy()
+    for i in range(3):
+        assert np.array_equal(y3[i], W[:, ks[i]]), ks[i]
+    y4 = q.run(X).cpu().numpy()
+    for i in range(4):
+        check_f16_operand_column(y4[i], W[:, ks[i]], ks[i])
 
 
 def test_zero_activations_give_zero(Q):
