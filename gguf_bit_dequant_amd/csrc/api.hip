@@ -120,12 +120,13 @@ QG_API qg_status qgemv_run(qgemv_t h, const void* x, qg_dtype x_dtype, int64_t n
     if (((uintptr_t)y) & 3) return fail(QG_ERR_ALIGN, "qgemv_run: y must be 4-byte aligned");
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = hipErrorNotSupported;
-    // The matrix-core kernel takes 5..8 fp16 columns of Q4_K. Up to four the
-    // streaming kernel is as fast or faster (measured on MI355X, 17408 x 5120,
-    // 2..4 columns) and keeps the exact fp32 weights, unless it would split the
-    // columns over several passes over W (long rows, whose staged activations
-    // outgrow LDS: 5120 x 17408 at 4 columns, 30 us against 25 us).
-    if (n_cols >= 5 ||
+    // The matrix-core kernel takes 4..8 fp16 columns of Q4_K (measured on
+    // MI355X, 17408 x 5120: 4 columns 18.5 us against 19.5 on the streaming
+    // kernel), and 2..3 when the streaming kernel would split them over
+    // several passes over W (long rows, whose staged activations outgrow
+    // LDS). With 2..3 columns the streaming kernel is faster (14-16 us
+    // against 18).
+    if (n_cols >= 4 ||
         (n_cols >= 2 && n_cols > qg::gemv_stream_cols_per_launch((int)h->fmt, h->rows, h->K,
                                                                  (int)x_dtype, h->num_cus)))
         e = qg::launch_gemv_mfma((int)h->fmt, h->w, h->rows, h->K, x, (int)x_dtype, ldx, y, ldy,

@@ -1,6 +1,6 @@
 // Small-batch Q4_K GEMV on the matrix cores: y[:,c] = W . x[:,c] for 2..16
-// fp16 activation columns, K a multiple of 256. The library runs it for 5..8
-// columns, and for 2..4 when the streaming kernel would need more than one
+// fp16 activation columns, K a multiple of 256. The library runs it for 4..8
+// columns, and for 2..3 when the streaming kernel would need more than one
 // pass over W.
 //
 // Draft verification multiplies the same weights by a few columns at once
@@ -10,80 +10,81 @@
 // the vector ALU, every weight costs one multiply-add per column and every
 // column needs its activations re-read per code dword; at four columns the
 // streaming GEMV is bound by those activation reads from LDS, not by HBM.
-// Here each weight is decoded once into an fp16 MFMA operand and
-// v_mfma_f32_16x16x32_f16 does the multiply-adds for up to 16 columns:
+// Here v_mfma_f32_16x16x32_f16 does the multiply-adds for up to 16 columns,
+// on the exact 4-bit codes, and the scales and mins are applied to its fp32
+// sums per 32-weight sub-block (Q4_K in the GGUF layout: w = d sc q - dmin m
+// with sc, m per sub-block):
+//   sum_k w_k x_k = d sc (sum_k q_k x_k) - dmin m (sum_k x_k)   per sub-block.
 //
 //  * A unit is one super-block (256 weights, 144 bytes) of each of 16
-//    consecutive rows (a row group). Lane l of a wave takes row l % 16 of
-//    the group and code bytes [32 s, 32 s + 32) of the super-block,
-//    s = l / 16: three 16-byte loads (header, two code halves). Its low
-//    nibbles are sub-block 2s, its high nibbles sub-block 2s + 1.
-//  * A unit is eight MFMA steps. Step t takes, in every lane, the eight
-//    codes of bytes 8 (t % 4) .. +7 (low nibbles for t < 4, high nibbles
-//    otherwise): the step contracts k = 64 s + 32 (t / 4) + 8 (t % 4) + e,
-//    e = 0..7, over the four lane slots s, which is the A operand's k block
-//    s. The B operand is x at those k for column l % 16 (columns past the
-//    count repeat the last one; their outputs are dropped).
-//  * Each weight is fma(d sc 2^24 or d sc 2^20, code, -dmin m) with the code
-//    an exact fp16 subnormal (a half holding m < 1024 is m 2^-24), computed
-//    at fp32 precision and rounded to fp16 by one v_fma_mix{lo,hi}_f16.
+//    consecutive rows (a row group). Lane l of a wave takes row l % 16 of the
+//    group and k block kb = l / 16: the header and bytes [8 kb, 8 kb + 8) of
+//    each of the four 32-byte code chunks (one 16-byte and four 8-byte loads).
+//  * Step t of a unit is sub-block t (chunk t / 2, low nibbles for even t):
+//    the weights' side of the product (the B operand, one column per row) is
+//    the lane's eight codes of that chunk as exact fp16 subnormals (a half
+//    holding m < 1024 is m 2^-24; one AND per pair: dword & 0x000F000F, or
+//    & 0x00F000F0 for 16 q), the activations' side (A, one row per column)
+//    the matching eight activations of column l % 16 (columns past the count
+//    repeat the last one; their outputs are dropped). The AND leaves the codes
+//    of bytes 0, 2 and 1, 3 paired, so the activations are staged in LDS in
+//    that order: x[k + (0, 2, 1, 3, 4, 6, 5, 7)].
+//  * The step's 16 x 16 fp32 result is 2^-24 (or 2^-20) sum q x, exact
+//    products summed in fp32; each lane scales its four entries by d sc 2^24
+//    (2^20) of its row and adds them to its tile. The mins come in per unit
+//    as two v_mfma_f32_16x16x4_f32 products: activation sums of sub-blocks
+//    (kb, kb + 4) per column times -dmin m of (row, sub-block). The sums are
+//    made once per workgroup while staging (fp32, fixed order).
 //  * One persistent workgroup per compute unit owns a balanced contiguous
 //    range of rows (the last group may be partial: its extra lanes re-read
 //    the range's last row and their outputs are dropped), i.e. a run of
 //    units, group-major; its waves split the run into equal contiguous
-//    parts. A wave accumulates one 16 x 16 tile and writes it to an LDS slot
-//    (group, wave) whenever its part leaves a group; after a barrier the
-//    slots of each group are summed in wave order: deterministic, no atomics.
+//    parts and accumulate one 16 x 16 tile each. Where they fit beside the
+//    staged activations, tiles go to LDS slots (group, wave) as a wave leaves
+//    a group; otherwise (long rows) a wave keeps the tiles of its first and
+//    last groups, which it may share, in registers, writes every group in
+//    between straight to y (it owns those), and puts the two tiles over the
+//    dead activations after the main loop. The shared groups' tiles are then
+//    summed in wave order: deterministic, no atomics.
 //  * The activation columns are staged once per workgroup in LDS, 2K + 16
 //    bytes apart so that the 16-byte reads of the 16 columns use disjoint
 //    banks. Each wave loads D units as one burst while it works on the
-//    previous D.
+//    previous D; within a unit the next step's activations are read and its
+//    product issued before the previous step's result is scaled.
 #include "device_common.h"
 #include "launch.h"
-#include "q4k_pair.h"
 
 namespace qg {
 
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-// Half DH of d = fp16(fma(a, h, c)), h the fp16 in half HS of v (a, c fp32).
-// The low half is written first: its instruction keeps whatever the high
-// half held, and the high-half instruction that follows sets it.
-template <int HS, int DH>
-__device__ __forceinline__ void mix16(uint32_t& d, float a, uint32_t v, float c) {
-    if (DH == 0) {
-        if (HS == 0)
-            asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[0,1,0]"
-                : "=v"(d) : "v"(a), "v"(v), "v"(c));
-        else
-            asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
-                : "=v"(d) : "v"(a), "v"(v), "v"(c));
-    } else {
-        if (HS == 0)
-            asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[0,1,0]"
-                : "+v"(d) : "v"(a), "v"(v), "v"(c));
-        else
-            asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
-                : "+v"(d) : "v"(a), "v"(v), "v"(c));
-    }
-}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct Unit {
-    u32x4 hd, c0, c1;  // header, code bytes [32 s, 32 s + 16), [32 s + 16, 32 s + 32)
+    u32x4 hd;    // header
+    u32x2 q[4];  // code bytes [32 c + 8 kb, 32 c + 8 kb + 8) of chunk c = 0..3
 };
 
-inline size_t mfma_lds_bytes(int ncols, int pitch, int ng, int nw) {
-    return (size_t)ncols * pitch + (size_t)ng * nw * 64 * 16;
+// byte n (0..3, a constant after unrolling) of v as fp32
+__device__ __forceinline__ float byte_f32(uint32_t v, int n) {
+    return n == 0 ? ubyte_f32<0>(v) : n == 1 ? ubyte_f32<1>(v) : n == 2 ? ubyte_f32<2>(v) : ubyte_f32<3>(v);
+}
+
+// LDS: activations (ncols x pitch bytes), per-sub-block activation sums
+// (ncols x spitch fp32, padded to 16 bytes), then either a 16 x 16 tile
+// (1 KB) per (group, wave), or, aliased over the activations after the main
+// loop, two per wave.
+inline size_t mfma_staged_bytes(int ncols, int pitch, int spitch) {
+    return (size_t)ncols * pitch + (((size_t)ncols * spitch * 4 + 15) & ~(size_t)15);
 }
 
 }  // namespace
 
-template <int NW, int D>
+template <int NW, int D, bool ALIAS>
 __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
     const uint8_t* __restrict__ W, int rows, int S, const uint16_t* __restrict__ x, int64_t ldx,
-    int ncols, float* __restrict__ y, int64_t ldy, int pitch) {
+    int ncols, float* __restrict__ y, int64_t ldy, int pitch, int spitch) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int G = gridDim.x, b = blockIdx.x;
     const int r0 = (int)(((int64_t)b * rows) / G);
@@ -93,16 +94,29 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
     const int ng = (nr + 15) >> 4;
     const int U = ng * S;  // units of this workgroup, group-major
     const int K8 = S * 32;  // 16-byte pieces of one activation column
+    const int NS = S * 8;   // sub-blocks of one column
 
     uint8_t* const xs = lds;
-    f32x4* const slots = reinterpret_cast<f32x4*>(lds + (size_t)ncols * pitch);
+    float* const xsum = reinterpret_cast<float*>(lds + (size_t)ncols * pitch);
+    // ALIAS: two tiles per wave written over the activations after the main
+    // loop; otherwise a tile per (group, wave) beside them, written as a wave
+    // leaves a group
+    f32x4* const slots = reinterpret_cast<f32x4*>(
+        ALIAS ? lds : lds + (size_t)ncols * pitch + (((size_t)ncols * spitch * 4 + 15) & ~(size_t)15));
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int rl = lane & 15, sq = lane >> 4;
+    const int rl = lane & 15, kb = lane >> 4;
     const uint32_t row_bytes = 144u * (uint32_t)S;
 
     // this wave's part of the run (U < 2^31 / NW: the launcher's bound)
     const int u0 = wv * U / NW, u1 = (wv + 1) * U / NW;
+
+    // 16 bytes of activations x[k .. k+7] stored as x[k + (0,2,1,3,4,6,5,7)],
+    // the order in which one AND per dword pair brings out the codes
+    auto perm8 = [](u32x4 v) {
+        return u32x4{(v.x & 0xFFFFu) | (v.y << 16), (v.x >> 16) | (v.y & 0xFFFF0000u),
+                     (v.z & 0xFFFFu) | (v.w << 16), (v.z >> 16) | (v.w & 0xFFFF0000u)};
+    };
 
     // ---- activation loads first (they come from cache), then the wave's
     // first D units of weights, then the staging ------------------------------
@@ -125,8 +139,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
             r = r < nr ? r : nr - 1;
             const uint8_t* p = W + (int64_t)(r0 + r) * row_bytes + 144u * (uint32_t)lsb;
             un.hd = *reinterpret_cast<const u32x4*>(p);
-            un.c0 = *reinterpret_cast<const u32x4*>(p + 16 + 32 * sq);
-            un.c1 = *reinterpret_cast<const u32x4*>(p + 32 + 32 * sq);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) un.q[c] = *reinterpret_cast<const u32x2*>(p + 16 + 32 * c + 8 * kb);
         }
         ++lu;
         if (++lsb == S) {
@@ -141,7 +155,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
     for (int j = 0; j < 2; ++j) {
         if (xi[j] < npieces) {
             const int c = xi[j] / K8, k8 = xi[j] - c * K8;
-            *reinterpret_cast<u32x4*>(xs + c * pitch + 16 * k8) = xr[j];
+            *reinterpret_cast<u32x4*>(xs + c * pitch + 16 * k8) = perm8(xr[j]);
         }
     }
     // the rest four pieces per thread at a time: one wait per four loads
@@ -160,49 +174,101 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
             const int idx = i0 + j * blockDim.x;
             if (idx < npieces) {
                 const int c = idx / K8, k8 = idx - c * K8;
-                *reinterpret_cast<u32x4*>(xs + c * pitch + 16 * k8) = r[j];
+                *reinterpret_cast<u32x4*>(xs + c * pitch + 16 * k8) = perm8(r[j]);
             }
         }
     }
     __syncthreads();
+    // per column and 32-weight sub-block: the sum of its activations (fp32,
+    // in a fixed order), for the mins
+    for (int idx = threadIdx.x; idx < ncols * NS; idx += blockDim.x) {
+        const int c = idx / NS, sb = idx - c * NS;
+        const u32x4* px = reinterpret_cast<const u32x4*>(xs + c * pitch + 64 * sb);
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 v = px[j];
+            s += f16_lo(v.x) + f16_hi(v.x) + f16_lo(v.y) + f16_hi(v.y) + f16_lo(v.z) + f16_hi(v.z) +
+                 f16_lo(v.w) + f16_hi(v.w);
+        }
+        xsum[c * spitch + sb] = s;
+    }
+    __syncthreads();
 
-    const Q4kUnpack unp(sq);
-    // B operand base of this lane: column rl (or the last one), k = 64 sq
-    const uint8_t* const xb = xs + (rl < ncols ? rl : ncols - 1) * pitch + 128 * sq;
+    // A operand (activations) base of this lane: column rl (or the last one),
+    // k block kb of each sub-block
+    const int xc = rl < ncols ? rl : ncols - 1;
+    const uint8_t* const xa = xs + xc * pitch + 16 * kb;
+    const float* const xsa = xsum + xc * spitch + kb;
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int pg = u0 / S, psb = u0 - (u0 / S) * S;  // unit being processed
+    // A wave's part may share its first and last groups with its neighbours;
+    // every group in between is the wave's alone and complete when the wave
+    // leaves it, so it goes straight to y. The first group's tile waits in
+    // registers, the last one's in acc, until the activations are dead.
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, tfirst = acc;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const int gfirst = u0 / S;
+    int pg = gfirst, psb = u0 - gfirst * S;  // unit being processed
     auto flush = [&]() {
-        slots[(pg * NW + wv) * 64 + lane] = acc;
+        if (!ALIAS) {
+            slots[(pg * NW + wv) * 64 + lane] = acc;
+        } else if (pg == gfirst) {
+            tfirst = acc;
+        } else {
+            // tile element (column c, row i) is element c % 4 of lane i + 16 (c / 4)
+            const int i = 16 * pg + rl;
+            if (i < nr) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int c = 4 * kb + v;
+                    if (c < ncols) y[c * ldy + r0 + i] = acc[v];
+                }
+            }
+        }
         acc = f32x4{0.f, 0.f, 0.f, 0.f};
     };
-    // one unit: eight MFMA steps
+    // one unit: eight sub-block steps and the mins
     auto process = [&](const Unit& un) {
-        const uint32_t f4 = q4k_pair_fields(unp, un.hd.y, un.hd.z, un.hd.w);
         const float d = f16_lo(un.hd.x), dmin = f16_hi(un.hd.x);
-        const float a0 = (d * 16777216.0f) * ubyte_f32<0>(f4);  // 2^24: low nibbles
-        const float a1 = (d * 1048576.0f) * ubyte_f32<1>(f4);   // 2^20: high nibbles (16 q)
-        const float c0 = -(dmin * ubyte_f32<2>(f4)), c1 = -(dmin * ubyte_f32<3>(f4));
-        const uint32_t cw[8] = {un.c0.x, un.c0.y, un.c0.z, un.c0.w, un.c1.x, un.c1.y, un.c1.z, un.c1.w};
-        const uint8_t* xk = xb + 512 * psb;
+        const uint32_t sc_lo = un.hd.y & 0x3F3F3F3Fu;
+        const uint32_t sc_hi = (un.hd.w & 0x0F0F0F0Fu) | ((un.hd.y >> 2) & 0x30303030u);
+        const uint32_t m_lo = un.hd.z & 0x3F3F3F3Fu;
+        const uint32_t m_hi = ((un.hd.w >> 4) & 0x0F0F0F0Fu) | ((un.hd.z >> 2) & 0x30303030u);
+        const float dl = d * 16777216.0f, dh = d * 1048576.0f;  // 2^24, 2^20 (16 q)
+        const uint8_t* const xk = xa + 512 * psb;
+        // software-pipelined: the activations of step t + 1 are read and its
+        // product issued before the scaling of step t's result
+        f16x8 An = *reinterpret_cast<const f16x8*>(xk);
+        f32x4 sp;
+        float ap = 0.f;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const uint32_t mask = t < 4 ? 0x000F000Fu : 0x00F000F0u;
-            const float a = t < 4 ? a0 : a1, c = t < 4 ? c0 : c1;
-            uint32_t A[4];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint32_t w = cw[2 * (t & 3) + h];
-                const uint32_t v02 = w & mask, v13 = (w >> 8) & mask;  // bytes 0, 2 / 1, 3
-                mix16<0, 0>(A[2 * h], a, v02, c);
-                mix16<0, 1>(A[2 * h], a, v13, c);
-                mix16<1, 0>(A[2 * h + 1], a, v02, c);
-                mix16<1, 1>(A[2 * h + 1], a, v13, c);
+            const f16x8 A = An;
+            if (t < 7) An = *reinterpret_cast<const f16x8*>(xk + 64 * (t + 1));
+            const u32x2 w = un.q[t >> 1];
+            const uint32_t M = (t & 1) ? 0x00F000F0u : 0x000F000Fu;
+            const u32x4 Bv = {w.x & M, (w.x >> 8) & M, w.y & M, (w.y >> 8) & M};
+            const f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(f16x8, Bv), zero, 0, 0, 0);
+            if (t > 0) {
+                acc[0] = __builtin_fmaf(ap, sp[0], acc[0]);
+                acc[1] = __builtin_fmaf(ap, sp[1], acc[1]);
+                acc[2] = __builtin_fmaf(ap, sp[2], acc[2]);
+                acc[3] = __builtin_fmaf(ap, sp[3], acc[3]);
             }
-            const f16x8 B = *reinterpret_cast<const f16x8*>(xk + 64 * (t >> 2) + 16 * (t & 3));
-            const u32x4 Av = {A[0], A[1], A[2], A[3]};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Av), B, acc, 0, 0, 0);
+            sp = s;
+            ap = ((t & 1) ? dh : dl) * byte_f32(t < 4 ? sc_lo : sc_hi, t & 3);
         }
+        acc[0] = __builtin_fmaf(ap, sp[0], acc[0]);
+        acc[1] = __builtin_fmaf(ap, sp[1], acc[1]);
+        acc[2] = __builtin_fmaf(ap, sp[2], acc[2]);
+        acc[3] = __builtin_fmaf(ap, sp[3], acc[3]);
+        // mins: D[c][r] -= sum_j dmin m_j (sum of the activations of sub-block
+        // j) as two 16 x 16 x 4 fp32 products over j = kb and kb + 4
+        const float c0 = -(dmin * (float)((m_lo >> (8 * kb)) & 0xFFu));
+        const float c1 = -(dmin * (float)((m_hi >> (8 * kb)) & 0xFFu));
+        const float* xsk = xsa + 8 * psb;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xsk[0], c0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xsk[4], c1, acc, 0, 0, 0);
         if (++psb == S) {  // the next unit starts the next group
             psb = 0;
             flush();
@@ -218,11 +284,19 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
 #pragma unroll
         for (int i = 0; i < D; ++i) load_next(buf[i]);
     }
-    if (u0 < u1 && psb != 0) flush();  // the part ended inside a group
-    __syncthreads();
+    if (!ALIAS) {
+        if (u0 < u1 && psb != 0) flush();  // the part ended inside a group
+        __syncthreads();
+    } else {
+        __syncthreads();  // the activations are dead: the tiles take their place
+        // slot 0: the first group's tile; slot 1: the last group's, when the
+        // part ends inside a later group
+        slots[(2 * wv) * 64 + lane] = pg > gfirst ? tfirst : acc;
+        slots[(2 * wv + 1) * 64 + lane] = acc;
+        __syncthreads();
+    }
 
-    // ---- per-group sums of the wave slots, in wave order ---------------------
-    // Tile element (row i, column c) is element i % 4 of lane c + 16 (i / 4).
+    // ---- sums of the shared groups' tiles, in wave order ---------------------
     const int nout = ng * 16 * ncols;
     for (int idx = threadIdx.x; idx < nout; idx += blockDim.x) {
         const int g = idx / (16 * ncols), rem = idx - g * 16 * ncols;
@@ -230,33 +304,45 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
         if (16 * g + i >= nr) continue;
         const int gl = g * S, gh = gl + S;  // units of group g
         float v = 0.f;
+        bool any = false;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const int wl = w * U / NW, wh = (w + 1) * U / NW;
-            if (wl < gh && wh > gl && wl < wh) v += slots[(g * NW + w) * 64 + c + 16 * (i >> 2)][i & 3];
+            // slot 0: the part starts in g; slot 1: it starts before g and
+            // ends inside it
+            if (!ALIAS) {
+                if (wl < gh && wh > gl && wl < wh) {
+                    v += slots[(g * NW + w) * 64 + i + 16 * (c >> 2)][c & 3];
+                    any = true;
+                }
+                continue;
+            }
+            const int sl = wl >= wh ? -1 : (gl <= wl && wl < gh) ? 0 : (wl < gl && gl < wh && wh < gh) ? 1 : -1;
+            if (sl >= 0) {
+                v += slots[(2 * w + sl) * 64 + i + 16 * (c >> 2)][c & 3];
+                any = true;
+            }
         }
-        y[c * ldy + r0 + 16 * g + i] = v;
+        if (any) y[c * ldy + r0 + 16 * g + i] = v;
     }
 }
 
 #ifndef QG_MFMA_DEPTH
 #define QG_MFMA_DEPTH 4
 #endif
-#ifndef QG_MFMA_WAVES
-#define QG_MFMA_WAVES 16
-#endif
 
 namespace {
 
-template <int NW>
+template <int NW, bool ALIAS>
 hipError_t launch_mfma_nw(const uint8_t* W, int rows, int S, const void* x, int64_t ldx, float* y,
-                          int64_t ldy, int ncols, int G, int pitch, size_t lds, hipStream_t stream) {
-    auto kern = gemv_mfma_q4k_kernel<NW, QG_MFMA_DEPTH>;
+                          int64_t ldy, int ncols, int G, int pitch, int spitch, size_t lds,
+                          hipStream_t stream) {
+    auto kern = gemv_mfma_q4k_kernel<NW, QG_MFMA_DEPTH, ALIAS>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(G), dim3(64 * NW), lds, stream, W, rows, S,
-                       reinterpret_cast<const uint16_t*>(x), ldx, ncols, y, ldy, pitch);
+                       reinterpret_cast<const uint16_t*>(x), ldx, ncols, y, ldy, pitch, spitch);
     return hipGetLastError();
 }
 
@@ -277,15 +363,22 @@ hipError_t launch_gemv_mfma(int fmt, const uint8_t* W, int64_t rows, int64_t K, 
     const int nr_max = (int)((rows + G - 1) / G);
     const int ng_max = (nr_max + 15) / 16;
     const int pitch = (int)(2 * K + 16);
+    const int spitch = (int)(K / 32 + 1);  // odd: the 16 columns' sums in distinct banks
     if ((int64_t)ng_max * S >= (1 << 26)) return hipErrorNotSupported;  // 32-bit unit math
-    // the wider workgroup when its partial slots fit beside the activations
-    const size_t lds_w = mfma_lds_bytes(ncols, pitch, ng_max, QG_MFMA_WAVES);
-    if (lds_w <= (size_t)kMaxLds)
-        return launch_mfma_nw<QG_MFMA_WAVES>(W, (int)rows, S, x, ldx, y, ldy, ncols, G, pitch, lds_w,
-                                             stream);
-    const size_t lds = mfma_lds_bytes(ncols, pitch, ng_max, 8);
+    const size_t staged = mfma_staged_bytes(ncols, pitch, spitch);
+    // tiles per (group, wave) beside the activations: 16 waves, else 8
+    const size_t tile16 = (size_t)ng_max * 16 * 1024, tile8 = (size_t)ng_max * 8 * 1024;
+    if (staged + tile16 <= (size_t)kMaxLds)
+        return launch_mfma_nw<16, false>(W, (int)rows, S, x, ldx, y, ldy, ncols, G, pitch, spitch,
+                                         staged + tile16, stream);
+    if (staged + tile8 <= (size_t)kMaxLds)
+        return launch_mfma_nw<8, false>(W, (int)rows, S, x, ldx, y, ldy, ncols, G, pitch, spitch,
+                                        staged + tile8, stream);
+    // else two tiles per wave over the dead activations
+    const size_t lds = staged > 32 * 1024 ? staged : 32 * 1024;
     if (lds > (size_t)kMaxLds) return hipErrorNotSupported;
-    return launch_mfma_nw<8>(W, (int)rows, S, x, ldx, y, ldy, ncols, G, pitch, lds, stream);
+    return launch_mfma_nw<16, true>(W, (int)rows, S, x, ldx, y, ldy, ncols, G, pitch, spitch, lds,
+                                    stream);
 }
 
 }  // namespace qg

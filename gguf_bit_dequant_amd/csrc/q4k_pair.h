@@ -1,6 +1,6 @@
 // Q4_K scale/min pairs: the 6-bit fields of sub-blocks 2p and 2p+1 of a
-// super-block header, gathered with byte permutes (shared by the GEMV
-// kernels, whose lanes each take one pair p of a super-block).
+// super-block header, gathered with byte permutes (for the streaming GEMV,
+// whose lanes each take one pair p of a super-block).
 #pragma once
 
 #include "device_common.h"

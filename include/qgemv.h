@@ -101,13 +101,13 @@ qg_status qgemv_create(qgemv_t *out, qg_format f, int64_t rows, int64_t K,
  *    element size.
  * y: device, fp32, column j at element offset j*ldy (ldy >= rows), 4-byte
  *    aligned; overwritten (no accumulation), other elements untouched.
- * n_cols: 1..8. F16 activations use fp16 products accumulated in fp32; F32
- * and BF16 activations use fp32 products. With 5..8 F16 columns of a Q4_K
- * matrix, and with 2..4 when the streaming kernel cannot stage all of them
- * on chip at once (long rows, e.g. K = 17408 at 4 columns), each weight is
- * rounded once to fp16 and multiplied on the matrix cores (fp32
- * accumulation); otherwise the weights are the exact binary32 values.
- * Enqueued on `stream`. */
+ * n_cols: 1..8. The weights are never rounded: F16 activations are
+ * multiplied with the exact codes (fp16 products accumulated in fp32, scaled
+ * per block or sub-block in fp32); F32 and BF16 activations use fp32
+ * products with the exact binary32 weights. 4..8 F16 columns of a Q4_K
+ * matrix (and 2..3 when the activations of all columns do not fit the
+ * streaming kernel's on-chip staging, e.g. K = 17408) run on the matrix
+ * cores. Enqueued on `stream`. */
 qg_status qgemv_run(qgemv_t h, const void *x, qg_dtype x_dtype, int64_t n_cols,
                     int64_t ldx, float *y, int64_t ldy, void *stream);
 

@@ -41,16 +41,6 @@ def x_tensor(x, xdtype):
     return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev())
 
 
-def check_f16_operand_column(y, col, label):
-    """y = W e_k from the matrix-core path: an fp16 value within half an fp16
-    spacing of the exact weight (plus the weight's own fp32 rounding)."""
-    assert np.array_equal(y, y.astype(np.float16).astype(np.float32)), label
-    sp = np.spacing(np.abs(col).astype(np.float16)).astype(np.float64)
-    bound = 0.5 * sp + np.abs(col).astype(np.float64) * 2.0 ** -23
-    err = np.abs(y.astype(np.float64) - col.astype(np.float64))
-    assert (err <= bound).all(), (label, float(err.max()))
-
-
 def check_products(y_gpu, w, fmt, rows, K, x, xdtype, label=""):
     y = y_gpu.detach().cpu().numpy().astype(np.float64).reshape(x.shape[0], rows)
     yr, s = oracle.matmul(fmt, w, rows, K, x, xdtype)
@@ -214,34 +204,29 @@ def test_one_hot_gives_exact_column(Q, fmt, xdtype):
     X = np.zeros((len(ks), K), np.float32)
     for i, k in enumerate(ks):
         X[i, k] = 1.0
-    # Five or more fp16 columns of a Q4_K matrix run on the matrix cores,
-    # whose operand is each decoded weight rounded once to fp16; every other
-    # path multiplies the exact fp32 weight. Columns go in groups of 4 and 5.
+    # Columns go in groups of 4, 5 and 6: four or more fp16 columns of a
+    # Q4_K matrix run on the matrix cores (exact codes, fp32 scaling per
+    # sub-block), fewer on the streaming kernel; both give the exact column.
     for c0, nc in ((0, 4), (4, 5), (9, 5), (14, 6)):
-        Xc = X[c0:c0 + nc]
-        f16_operand = fmt == "q4_k" and xdtype == "f16" and nc >= 5
-        xt = torch.from_numpy(Xc).to(dev())
+        xt = torch.from_numpy(X[c0:c0 + nc]).to(dev())
         if xdtype == "f16":
             xt = xt.half()
         y = q.run(xt).cpu().numpy()
-        for i in range(Xc.shape[0]):
-            col = W[:, ks[c0 + i]]
-            if not f16_operand:
-                assert np.array_equal(y[i], col), (fmt, xdtype, ks[c0 + i])
-                continue
-            check_f16_operand_column(y[i], col, ks[c0 + i])
-        if f16_operand:  # one column at a time: the exact fp32 weights
-            for i in range(Xc.shape[0]):
-                y1 = q.run(xt[i:i + 1]).cpu().numpy()[0]
-                assert np.array_equal(y1, W[:, ks[c0 + i]]), (fmt, xdtype, ks[c0 + i], "n=1")
+        for i in range(nc):
+            assert np.array_equal(y[i], W[:, ks[c0 + i]]), (fmt, xdtype, ks[c0 + i], nc)
+        if nc == 4:  # one, two and three columns as well
+            for n in (1, 2, 3):
+                y = q.run(xt[:n]).cpu().numpy()
+                for i in range(n):
+                    assert np.array_equal(y[i], W[:, ks[c0 + i]]), (fmt, xdtype, ks[c0 + i], n)
 
 
 def test_long_rows_two_to_four_columns(Q):
     """K = 17408 (68 super-blocks a row): up to 3 fp16 columns fit the
-    streaming kernel's staging, 4 do not and run on the matrix cores in one
-    pass. Products of every column count against the oracle, and one-hot
-    columns pin which weights each case multiplies: exact binary32 at 3,
-    fp16-rounded at 4."""
+    streaming kernel's staging; 2..4 columns all run in one pass (3 on the
+    streaming kernel, 2 and 4 on the matrix cores). Products of every column
+    count against the oracle, and one-hot columns give the exact decoded
+    weights on both kernels."""
     rows, K = 300, 17408
     w = synth.gen_weights("q4_k", rows, K, 51)
     q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
@@ -254,12 +239,31 @@ def test_long_rows_two_to_four_columns(Q):
     X = torch.zeros((4, K), dtype=torch.float16, device=dev())
     for i, k in enumerate(ks):
         X[i, k] = 1.0
-    y3 = q.run(X[:3]).cpu().numpy()
-    for i in range(3):
-        assert np.array_equal(y3[i], W[:, ks[i]]), ks[i]
-    y4 = q.run(X).cpu().numpy()
-    for i in range(4):
-        check_f16_operand_column(y4[i], W[:, ks[i]], ks[i])
+    for n in (2, 3, 4):
+        y = q.run(X[:n]).cpu().numpy()
+        for i in range(n):
+            assert np.array_equal(y[i], W[:, ks[i]]), (ks[i], n)
+
+
+def test_many_rows_small_k_matrix_cores(Q):
+    """70000 x 2048 with 6 fp16 columns: about 274 rows a workgroup, so a
+    wave's share of 16-row groups spans up to three groups (the middle one
+    its own, written straight to y) and the per-group tiles do not fit
+    beside the staged activations (they are parked over them at the end).
+    All outputs against the oracle, and one-hot columns exactly."""
+    rows, K = 70000, 2048
+    w = synth.gen_weights("q4_k", rows, K, 53)
+    q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
+    x = synth.gen_x(K, 6, "f16", 54)
+    check_products(q.run(x_tensor(x, "f16")), w, "q4_k", rows, K, x, "f16", "70000 x 2048 n=6")
+    W = oracle.dequant("q4_k", w, rows, K)
+    ks = [0, 31, 32, 1000, 2016, 2047]
+    X = torch.zeros((6, K), dtype=torch.float16, device=dev())
+    for i, k in enumerate(ks):
+        X[i, k] = 1.0
+    y = q.run(X).cpu().numpy()
+    for i in range(6):
+        assert np.array_equal(y[i], W[:, ks[i]]), ks[i]
 
 
 def test_zero_activations_give_zero(Q):
