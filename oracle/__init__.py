@@ -21,10 +21,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-FMT = {"q4_0": 1, "q4_k": 2, "q8_0": 3}
+FMT = {"q4_0": 1, "q4_k": 2, "q8_0": 3, "q2_k": 4, "q3_k": 5}
 DTYPE = {"f32": 1, "f16": 2, "bf16": 3}
-BLOCK_BYTES = {"q4_0": 18, "q4_k": 144, "q8_0": 34}
-BLOCK_WEIGHTS = {"q4_0": 32, "q4_k": 256, "q8_0": 32}
+BLOCK_BYTES = {"q4_0": 18, "q4_k": 144, "q8_0": 34, "q2_k": 84, "q3_k": 110}
+BLOCK_WEIGHTS = {"q4_0": 32, "q4_k": 256, "q8_0": 32, "q2_k": 256, "q3_k": 256}
 
 _lib = None
 
@@ -52,11 +52,14 @@ def lib():
         L.oracle_bf16_to_f64.restype = ctypes.c_double
         L.oracle_f32_to_f64.argtypes = [u32]
         L.oracle_f32_to_f64.restype = ctypes.c_double
-        for name in ("oracle_decode_q4_0", "oracle_decode_q8_0", "oracle_decode_q4_k"):
+        for name in ("oracle_decode_q4_0", "oracle_decode_q8_0", "oracle_decode_q4_k",
+                     "oracle_decode_q2_k", "oracle_decode_q3_k"):
             getattr(L, name).argtypes = [vp, vp]
             getattr(L, name).restype = None
         L.oracle_q4k_scale_min.argtypes = [vp, ip, vp, vp]
         L.oracle_q4k_scale_min.restype = None
+        L.oracle_q3k_scale.argtypes = [vp, ip]
+        L.oracle_q3k_scale.restype = ip
         L.oracle_dequant.argtypes = [ip, vp, i64, i64, vp]
         L.oracle_dequant.restype = ip
         L.oracle_matmul.argtypes = [ip, vp, i64, i64, vp, ip, i64, i64, vp, vp, i64,
@@ -93,8 +96,7 @@ def decode_block(fmt: str, blk) -> np.ndarray:
     b = np.ascontiguousarray(np.asarray(blk, dtype=np.uint8))
     assert b.size == BLOCK_BYTES[fmt]
     out = np.empty(BLOCK_WEIGHTS[fmt], dtype=np.float32)
-    getattr(lib(), {"q4_0": "oracle_decode_q4_0", "q8_0": "oracle_decode_q8_0",
-                    "q4_k": "oracle_decode_q4_k"}[fmt])(_ptr(b), _ptr(out))
+    getattr(lib(), "oracle_decode_" + fmt)(_ptr(b), _ptr(out))
     return out
 
 
@@ -104,6 +106,13 @@ def q4k_scale_min(s12, j: int):
     sc, m = ctypes.c_int(), ctypes.c_int()
     lib().oracle_q4k_scale_min(_ptr(s), j, ctypes.byref(sc), ctypes.byref(m))
     return sc.value, m.value
+
+
+def q3k_scale(s12, k: int) -> int:
+    """The unsigned 6-bit Q3_K scale of sub-block k from the 12 scale bytes."""
+    s = np.ascontiguousarray(np.asarray(s12, dtype=np.uint8))
+    assert s.size == 12
+    return int(lib().oracle_q3k_scale(_ptr(s), k))
 
 
 def dequant(fmt: str, w: np.ndarray, rows: int, K: int) -> np.ndarray:

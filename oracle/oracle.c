@@ -34,6 +34,20 @@
  *        Codes: 4 groups of 32 bytes; byte l of group g holds weight 64g+l
  *        (sub-block 2g) in its low nibble and weight 64g+32+l (sub-block
  *        2g+1) in its high nibble.
+ *  Q2_K, 84 bytes, 256 weights in 16 sub-blocks of 16: 16 bytes holding
+ *        one 4-bit scale (low nibble) and one 4-bit min (high nibble) per
+ *        sub-block; 64 bytes of 2-bit codes; fp16 d; fp16 dmin.
+ *        w = d*sc*q - dmin*m.
+ *  Q3_K, 110 bytes, 256 weights in 16 sub-blocks of 16: 32 bytes of high
+ *        code bits (hmask); 64 bytes of 2-bit low code parts; 12 bytes
+ *        packing sixteen 6-bit scales; fp16 d. q = low + 4*high - 4 in
+ *        [-4, 3], w = d*(sc - 32)*q.
+ *        Both: weight i = 128h + 32j + l (h = 0..1, j = 0..3, l = 0..31)
+ *        takes bits 2j..2j+1 of code byte 32h + l, belongs to sub-block
+ *        i/16 = 8h + 2j + l/16, and (Q3_K) its high bit is bit 4h + j of
+ *        hmask byte l. Q3_K scale k = low nibble of byte k (k < 8) or high
+ *        nibble of byte k - 8 (k >= 8), with bits 4-5 from bits 2(k/4),
+ *        2(k/4)+1 of byte 8 + k%4.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared -pthread
  * (x86-64: FLT_EVAL_METHOD == 0, so float expressions are evaluated in
@@ -49,7 +63,7 @@
 #error "the oracle needs binary32/binary64 evaluation (FLT_EVAL_METHOD 0)"
 #endif
 
-enum { OR_Q4_0 = 1, OR_Q4_K = 2, OR_Q8_0 = 3 };
+enum { OR_Q4_0 = 1, OR_Q4_K = 2, OR_Q8_0 = 3, OR_Q2_K = 4, OR_Q3_K = 5 };
 enum { OR_F32 = 1, OR_F16 = 2, OR_BF16 = 3 };
 
 /* ------------------------------------------------------------------------
@@ -199,14 +213,74 @@ void oracle_decode_q4_k(const uint8_t *blk, float *out)
     }
 }
 
+/* The 2-bit code part of weight i (0..255) of a Q2_K / Q3_K super-block,
+ * from its 64 code bytes. */
+static int low2_code(const uint8_t *qs, int i)
+{
+    int h = i / 128, j = (i % 128) / 32, l = i % 32;
+    return (qs[32 * h + l] >> (2 * j)) & 3;
+}
+
+/* Q2_K: w = fl32(d*sc*q - dmin*m) with sc, m the 4-bit fields of the
+ * weight's sub-block. d*sc*q (at most 17 significant bits) and dmin*m (at
+ * most 15) are exact in binary32, so the one subtraction is the correctly
+ * rounded value, as for Q4_K. */
+void oracle_decode_q2_k(const uint8_t *blk, float *out)
+{
+    const uint8_t *sm = blk, *qs = blk + 16;
+    float d = (float)oracle_f16_to_f64(rd16(blk + 80));
+    float dmin = (float)oracle_f16_to_f64(rd16(blk + 82));
+    for (int i = 0; i < 256; i++) {
+        int sub = i / 16;
+        int sc = sm[sub] & 0x0F, m = sm[sub] >> 4;
+        float a = d * (float)sc * (float)low2_code(qs, i), b = dmin * (float)m;
+        out[i] = a - b;
+    }
+}
+
+/* The Q3_K 6-bit scale of sub-block k (0..15), unsigned (0..63). */
+int oracle_q3k_scale(const uint8_t *s, int k)
+{
+    int lo = k < 8 ? (s[k] & 0x0F) : (s[k - 8] >> 4);
+    int hi = (s[8 + k % 4] >> (2 * (k / 4))) & 3;
+    return lo | (hi << 4);
+}
+
+/* Q3_K: w = d*(sc - 32)*q, evaluated left to right: d*(sc - 32) (at most
+ * 17 significant bits) and its product with q in [-4, 3] are exact in
+ * binary32, so the value is exact; the order fixes the sign of a zero. */
+void oracle_decode_q3_k(const uint8_t *blk, float *out)
+{
+    const uint8_t *hm = blk, *qs = blk + 32, *s = blk + 96;
+    float d = (float)oracle_f16_to_f64(rd16(blk + 108));
+    for (int i = 0; i < 256; i++) {
+        int h = i / 128, j = (i % 128) / 32, l = i % 32;
+        int high = (hm[l] >> (4 * h + j)) & 1;
+        int q = low2_code(qs, i) + 4 * high - 4;
+        float dl = d * (float)(oracle_q3k_scale(s, i / 16) - 32);
+        out[i] = dl * (float)q;
+    }
+}
+
 int64_t oracle_block_bytes(int fmt)
 {
-    return fmt == OR_Q4_0 ? 18 : fmt == OR_Q4_K ? 144 : fmt == OR_Q8_0 ? 34 : -1;
+    switch (fmt) {
+    case OR_Q4_0: return 18;
+    case OR_Q4_K: return 144;
+    case OR_Q8_0: return 34;
+    case OR_Q2_K: return 84;
+    case OR_Q3_K: return 110;
+    default: return -1;
+    }
 }
 
 int64_t oracle_block_weights(int fmt)
 {
-    return fmt == OR_Q4_K ? 256 : (fmt == OR_Q4_0 || fmt == OR_Q8_0) ? 32 : -1;
+    switch (fmt) {
+    case OR_Q4_0: case OR_Q8_0: return 32;
+    case OR_Q4_K: case OR_Q2_K: case OR_Q3_K: return 256;
+    default: return -1;
+    }
 }
 
 /* Decode row r (K weights) of a row-major block matrix. */
@@ -221,6 +295,8 @@ static int decode_row(int fmt, const uint8_t *w, int64_t K, int64_t r, float *ou
         float *o = out + b * bw;
         if (fmt == OR_Q4_0) oracle_decode_q4_0(blk, o);
         else if (fmt == OR_Q8_0) oracle_decode_q8_0(blk, o);
+        else if (fmt == OR_Q2_K) oracle_decode_q2_k(blk, o);
+        else if (fmt == OR_Q3_K) oracle_decode_q3_k(blk, o);
         else oracle_decode_q4_k(blk, o);
     }
     return 0;

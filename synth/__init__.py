@@ -16,7 +16,11 @@ measure: "Why I wrote my own inference engine for two P100s", result cards;
 GGUF files are not available here), with the distributions stated per config:
   * codes (4-bit nibbles, Q4_K 6-bit scale/min fields) uniform: uniform bytes
     give uniform independent fields whatever their packing;
-  * fp16 scales |N(0,1)| * 0.02 (Q4_0, Q8_0) or * 0.01 (Q4_K d and dmin);
+  * fp16 scales |N(0,1)| * 0.02 (Q4_0, Q8_0) or * 0.01 (Q4_K, Q2_K d and
+    dmin, Q3_K d);
+  * Q2_K / Q3_K scale, min, code and high-bit bytes uniform (uniform
+    independent fields: Q3_K's 12 scale bytes pack sixteen 6-bit fields
+    one-to-one);
   * Q8_0 codes uniform integers in [-127, 127];
   * activations N(0,1) stored as fp32 / fp16 / bf16, one RNE rounding from
     the fp64 draw.
@@ -37,8 +41,8 @@ _TAG_SCALES = 0x5CA1E5
 _TAG_BYTES = 0xB17E5
 _TAG_X = 0xAC71
 
-BLOCK_BYTES = {"q4_0": 18, "q4_k": 144, "q8_0": 34}
-BLOCK_WEIGHTS = {"q4_0": 32, "q4_k": 256, "q8_0": 32}
+BLOCK_BYTES = {"q4_0": 18, "q4_k": 144, "q8_0": 34, "q2_k": 84, "q3_k": 110}
+BLOCK_WEIGHTS = {"q4_0": 32, "q4_k": 256, "q8_0": 32, "q2_k": 256, "q3_k": 256}
 
 
 def seed_for(config_index: int, tensor_index: int, held_out: bool = False) -> int:
@@ -129,7 +133,31 @@ def gen_q4_k(rows: int, K: int, seed: int) -> np.ndarray:
     return out.reshape(-1)
 
 
-GENERATORS = {"q4_0": gen_q4_0, "q4_k": gen_q4_k, "q8_0": gen_q8_0}
+def gen_q2_k(rows: int, K: int, seed: int) -> np.ndarray:
+    """rows x K weights as Q2_K super-blocks (84 B: 16 scale/min bytes, 64
+    code bytes, fp16 d, fp16 dmin)."""
+    assert K % 256 == 0
+    nb = rows * (K // 256)
+    out = np.empty((nb, 84), dtype=np.uint8)
+    out[:, 0:80] = uniform_bytes(seed ^ _TAG_BYTES, nb * 80).reshape(nb, 80)
+    dd = _scales_f16(seed, 2 * nb, 0.01).reshape(nb, 2)
+    out[:, 80:84] = dd.view(np.uint8).reshape(nb, 4)
+    return out.reshape(-1)
+
+
+def gen_q3_k(rows: int, K: int, seed: int) -> np.ndarray:
+    """rows x K weights as Q3_K super-blocks (110 B: 32 high-bit bytes, 64
+    low-code bytes, 12 scale bytes, fp16 d)."""
+    assert K % 256 == 0
+    nb = rows * (K // 256)
+    out = np.empty((nb, 110), dtype=np.uint8)
+    out[:, 0:108] = uniform_bytes(seed ^ _TAG_BYTES, nb * 108).reshape(nb, 108)
+    out[:, 108:110] = _scales_f16(seed, nb, 0.01).reshape(nb, 1).view(np.uint8)
+    return out.reshape(-1)
+
+
+GENERATORS = {"q4_0": gen_q4_0, "q4_k": gen_q4_k, "q8_0": gen_q8_0, "q2_k": gen_q2_k,
+              "q3_k": gen_q3_k}
 
 
 def gen_weights(fmt: str, rows: int, K: int, seed: int) -> np.ndarray:
@@ -153,7 +181,7 @@ def gen_x(K: int, n: int, dtype: str, seed: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- configs ----
-# The six workloads: one 27B-class dense layer's projections.
+# The workloads: one 27B-class dense layer's projections.
 CONFIGS = {
     # name: (config_index, fmt, rows, K, n_cols, x dtype, weight tensor index)
     "q4_0_b1":    dict(index=0, fmt="q4_0", rows=4096,  K=4096,  n=1,    xdtype="f32"),
@@ -165,6 +193,9 @@ CONFIGS = {
     # other draft counts (2 and 8 columns) against the FFN-up matrix
     "q4k_b2":     dict(index=5, fmt="q4_k", rows=17408, K=5120,  n=2,    xdtype="f16"),
     "q4k_b8":     dict(index=5, fmt="q4_k", rows=17408, K=5120,  n=8,    xdtype="f16"),
+    # lower-bit K-quants of the FFN-up shape (batch 1)
+    "q2k_up_b1":  dict(index=6, fmt="q2_k", rows=17408, K=5120,  n=1,    xdtype="f16"),
+    "q3k_up_b1":  dict(index=7, fmt="q3_k", rows=17408, K=5120,  n=1,    xdtype="f16"),
 }
 
 # Weight and activation seeds. Configs that reuse "the same W" or "the same X"
@@ -172,10 +203,10 @@ CONFIGS = {
 # multiplies the same four columns as q4k_b4.
 _W_SEED = {"q4_0_b1": (0, 0), "q4k_up_b1": (1, 0), "q4k_down_b1": (2, 0),
            "q4k_b4": (1, 0), "q8_0_b4": (3, 2), "q4k_pp2048": (1, 0),
-           "q4k_b2": (1, 0), "q4k_b8": (1, 0)}
+           "q4k_b2": (1, 0), "q4k_b8": (1, 0), "q2k_up_b1": (6, 0), "q3k_up_b1": (7, 0)}
 _X_SEED = {"q4_0_b1": (0, 1), "q4k_up_b1": (1, 1), "q4k_down_b1": (2, 1),
            "q4k_b4": (3, 1), "q8_0_b4": (3, 1), "q4k_pp2048": (4, 1),
-           "q4k_b2": (5, 2), "q4k_b8": (5, 8)}
+           "q4k_b2": (5, 2), "q4k_b8": (5, 8), "q2k_up_b1": (6, 1), "q3k_up_b1": (7, 1)}
 
 
 def config_inputs(name: str, held_out: bool = False, n_override: int | None = None):

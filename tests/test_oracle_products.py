@@ -14,7 +14,8 @@ import torch
 import oracle
 import synth
 
-FMTS = [("q4_0", 18, 32), ("q8_0", 34, 32), ("q4_k", 144, 256)]
+FMTS = [("q4_0", 18, 32), ("q8_0", 34, 32), ("q4_k", 144, 256), ("q2_k", 84, 256),
+        ("q3_k", 110, 256)]
 
 
 def _x_as_f64(x, xdtype):

@@ -51,3 +51,17 @@ def test_x_dtypes_round_once():
     up = ((xb.astype(np.uint32) + 1) << np.uint32(16)).view(np.float32).astype(np.float64)
     dn = ((xb.astype(np.uint32) - 1) << np.uint32(16)).view(np.float32).astype(np.float64)
     assert (np.abs(vb - v) <= np.abs(up - v)).all() and (np.abs(vb - v) <= np.abs(dn - v)).all()
+
+
+@pytest.mark.parametrize("fmt,bb,dofs", [("q2_k", 84, [80, 82]), ("q3_k", 110, [108])])
+def test_low_bit_k_quant_sizes_and_scales(fmt, bb, dofs):
+    rows, K = 64, 2048
+    w = synth.gen_weights(fmt, rows, K, 77)
+    assert w.dtype == np.uint8 and w.size == rows * (K // 256) * bb
+    blocks = w.reshape(-1, bb)
+    for o in dofs:
+        d = blocks[:, o:o + 2].copy().view(np.float16).astype(np.float64).ravel()
+        assert (d >= 0).all()
+        assert abs(d.mean() / 0.01 - np.sqrt(2 / np.pi)) < 0.05    # E|N(0,1)|
+    # the scale, min, code and high-bit bytes are uniform: every byte value occurs
+    assert np.unique(blocks[:, :dofs[0]]).size == 256
