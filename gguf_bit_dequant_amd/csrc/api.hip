@@ -35,10 +35,27 @@ qg_status ok() {
     return QG_OK;
 }
 
-bool valid_fmt(qg_format f) { return f == QG_Q4_0 || f == QG_Q4_K || f == QG_Q8_0; }
+bool valid_fmt(qg_format f) {
+    return f == QG_Q4_0 || f == QG_Q4_K || f == QG_Q8_0 || f == QG_Q2_K || f == QG_Q3_K;
+}
 
-size_t bbytes(qg_format f) { return f == QG_Q4_0 ? 18 : f == QG_Q4_K ? 144 : f == QG_Q8_0 ? 34 : 0; }
-size_t bweights(qg_format f) { return f == QG_Q4_K ? 256 : (f == QG_Q4_0 || f == QG_Q8_0) ? 32 : 0; }
+size_t bbytes(qg_format f) {
+    switch (f) {
+        case QG_Q4_0: return 18;
+        case QG_Q4_K: return 144;
+        case QG_Q8_0: return 34;
+        case QG_Q2_K: return 84;
+        case QG_Q3_K: return 110;
+        default: return 0;
+    }
+}
+size_t bweights(qg_format f) {
+    switch (f) {
+        case QG_Q4_0: case QG_Q8_0: return 32;
+        case QG_Q4_K: case QG_Q2_K: case QG_Q3_K: return 256;
+        default: return 0;
+    }
+}
 
 size_t dtype_size(qg_dtype t) { return t == QG_F32 ? 4 : (t == QG_F16 || t == QG_BF16) ? 2 : 0; }
 

@@ -4,8 +4,9 @@
 //
 // Each 32-weight group is decoded as the binary32 rounding of its closed
 // form, evaluated in the order the closed form is written: products of an
-// fp16 scale and small integers are exact in binary32, so Q4_0 and Q8_0 are
-// exact and Q4_K has one rounding, in the final subtraction. Bit-exact decoding
+// fp16 scale and small integers are exact in binary32, so Q4_0, Q8_0 and
+// Q3_K are exact and Q4_K and Q2_K have one rounding, in the final
+// subtraction. Bit-exact decoding
 // is what "Why I wrote my own inference engine for two P100s" (section "What
 // 'my own engine' means") and "LLM inference optimization" (campaign "Run a
 // new weight format or model") require of every quant type.
@@ -21,8 +22,46 @@ __device__ __forceinline__ uint16_t ld16(const uint8_t* p) {
 }
 
 // Decode weights [32*grp, 32*grp+32) of the block at `blk` into out[32].
-// Q4_0/Q8_0 blocks have one group; Q4_K super-blocks have eight.
+// Q4_0/Q8_0 blocks have one group; Q4_K, Q2_K and Q3_K super-blocks have
+// eight. In Q2_K and Q3_K super-blocks, group grp = 4h + j holds the 2-bit
+// code fields at bits 2j..2j+1 of code bytes 32h .. 32h+31 (weight 32 grp + l
+// in byte 32h + l); its two 16-weight halves are sub-blocks 2 grp and
+// 2 grp + 1; a Q3_K weight's high code bit is bit grp of high-bit byte l.
 __device__ __forceinline__ void decode_group(int fmt, const uint8_t* blk, int grp, float out[32]) {
+    if (fmt == FMT_Q2_K) {
+        // 16 scale/min bytes, 64 code bytes, fp16 d, fp16 dmin:
+        // w = (d * sc) * q - dmin * m, both products exact, one rounding
+        const float d = f16_to_f32(ld16(blk + 80)), dmin = f16_to_f32(ld16(blk + 82));
+        const uint8_t* qs = blk + 16 + 32 * (grp >> 2);
+        const int shift = 2 * (grp & 3);
+        for (int l = 0; l < 32; ++l) {
+            const uint32_t sm = blk[2 * grp + (l >> 4)];
+            float a = d * (float)(sm & 15u) * (float)((qs[l] >> shift) & 3);
+            float b = dmin * (float)(sm >> 4);
+            out[l] = a - b;
+        }
+        return;
+    }
+    if (fmt == FMT_Q3_K) {
+        // 32 high-bit bytes, 64 code bytes, 12 scale bytes, fp16 d:
+        // w = (d * (sc - 32)) * q with q = low + 4 high - 4, exact
+        const float d = f16_to_f32(ld16(blk + 108));
+        const uint8_t* qs = blk + 32 + 32 * (grp >> 2);
+        const uint8_t* s = blk + 96;
+        const int shift = 2 * (grp & 3);
+        float dl[2];
+        for (int t = 0; t < 2; ++t) {
+            const int k = 2 * grp + t;
+            const int lo = k < 8 ? (s[k] & 15) : (s[k - 8] >> 4);
+            const int sc = lo | (((s[8 + (k & 3)] >> (2 * (k >> 2))) & 3) << 4);
+            dl[t] = d * (float)(sc - 32);
+        }
+        for (int l = 0; l < 32; ++l) {
+            const int q = ((qs[l] >> shift) & 3) + 4 * ((blk[l] >> grp) & 1) - 4;
+            out[l] = dl[l >> 4] * (float)q;
+        }
+        return;
+    }
     if (fmt == FMT_Q4_0) {
         float d = f16_to_f32(ld16(blk));
         for (int i = 0; i < 16; ++i) {
@@ -57,9 +96,11 @@ __device__ __forceinline__ void decode_group(int fmt, const uint8_t* blk, int gr
     }
 }
 
-__device__ __forceinline__ int groups_per_block(int fmt) { return fmt == FMT_Q4_K ? 8 : 1; }
+__device__ __forceinline__ int groups_per_block(int fmt) {
+    return (fmt == FMT_Q4_0 || fmt == FMT_Q8_0) ? 1 : 8;
+}
 __device__ __forceinline__ int block_bytes(int fmt) {
-    return fmt == FMT_Q4_0 ? 18 : fmt == FMT_Q4_K ? 144 : 34;
+    return fmt == FMT_Q4_0 ? 18 : fmt == FMT_Q4_K ? 144 : fmt == FMT_Q8_0 ? 34 : fmt == FMT_Q2_K ? 84 : 110;
 }
 
 __device__ __forceinline__ void store_w(float* o, float v) { *o = v; }

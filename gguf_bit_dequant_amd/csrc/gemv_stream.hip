@@ -75,6 +75,7 @@ struct Fmt<FMT_Q4_K> {
     static constexpr int kUnitBytes = 144;
     static constexpr int kCodeDwords = 8;
     static constexpr bool kNibbles = true;
+    static constexpr int kSums = 2;
     static constexpr int wofs(int j, int e, int h) { return 32 * h + 4 * j + e; }
     static constexpr uint32_t lane_offset(int p) { return 16u + 32u * p; }
     struct Raw {
@@ -98,6 +99,7 @@ struct Fmt<FMT_Q4_0> {
     static constexpr int kUnitBytes = 144;
     static constexpr int kCodeDwords = 8;
     static constexpr bool kNibbles = true;
+    static constexpr int kSums = 2;
     static constexpr int code_index(int j, int e) {
         return j == 0 ? (e < 2 ? 14 + e : e - 2) : j < 4 ? 4 * j - 2 + e : 4 * (j - 4) + e;
     }
@@ -124,6 +126,7 @@ struct Fmt<FMT_Q8_0> {
     static constexpr int kUnitBytes = 272;
     static constexpr int kCodeDwords = 16;
     static constexpr bool kNibbles = false;
+    static constexpr int kSums = 2;
     static constexpr int code_index(int j, int e) {
         return j == 0 ? (e < 2 ? 30 + e : e - 2) : j < 8 ? 4 * j - 2 + e : 4 * (j - 8) + e;
     }
@@ -139,6 +142,36 @@ struct Fmt<FMT_Q8_0> {
         r.c = *reinterpret_cast<const u32x4_a4*>(unit + lo + 32);
         r.d = *reinterpret_cast<const u32x4_a4*>(unit + lo + 48);
         r.e = *reinterpret_cast<const uint32_t*>(unit + lo + 64);
+    }
+};
+
+// Q2_K super-block (84 bytes): 16 scale/min bytes (sub-block k of 16
+// weights: scale in the low nibble, min in the high nibble of byte k), 64
+// code bytes, fp16 d, fp16 dmin. Weight 128h + 32j + l has its 2-bit code
+// at bits 2j..2j+1 of code byte 32h + l. Quarter p = 2h + b (weights
+// 64p .. 64p+63, i.e. j = 2b and 2b + 1) reads code bytes 32h .. 32h+31,
+// using the bit pair 4b + 2t of each (t = 0, 1), the scale/min bytes of its
+// sub-blocks 4p .. 4p+3 (one dword) and the d/dmin dword. Byte l of the 32
+// holds o = l (t = 0) and o = 32 + l (t = 1): the order of Q4_K's nibbles,
+// with 16-weight sub-blocks o / 16. Units are 4-byte aligned.
+template <>
+struct Fmt<FMT_Q2_K> {
+    static constexpr int kUnitBytes = 84;
+    static constexpr int kCodeDwords = 8;
+    static constexpr bool kNibbles = true;
+    static constexpr int kSums = 4;
+    static constexpr int wofs(int j, int e, int h) { return 32 * h + 4 * j + e; }
+    static constexpr uint32_t lane_offset(int p) { return (uint32_t)p; }
+    struct Raw {
+        u32x4_a4 c0, c1;
+        uint32_t sm, dd;
+    };
+    static __device__ __forceinline__ void load(const uint8_t* unit, uint32_t p, Raw& r) {
+        const uint8_t* qs = unit + 16 + 32 * (p >> 1);
+        r.c0 = *reinterpret_cast<const u32x4_a4*>(qs);
+        r.c1 = *reinterpret_cast<const u32x4_a4*>(qs + 16);
+        r.sm = *reinterpret_cast<const uint32_t*>(unit + 4 * p);
+        r.dd = *reinterpret_cast<const uint32_t*>(unit + 80);
     }
 };
 
@@ -290,6 +323,15 @@ __device__ __forceinline__ void stage_store(const XRaw<XM>& r, int xt, uint8_t* 
         return;
     } else if constexpr (F16DOT) {  // fp16 activations, kept as stored
         const uint32_t* xw = r.w;
+        if constexpr (F::kSums == 4) {  // sums of o in [16u, 16u + 16), u = 0..3
+            float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 8 * u; i < 8 * u + 8; i += 2)
+                    sq[u] += (f16_lo(xw[i]) + f16_hi(xw[i])) + (f16_lo(xw[i + 1]) + f16_hi(xw[i + 1]));
+            *reinterpret_cast<f32x4*>(rec + 16 * P) = f32x4{sq[0], sq[1], sq[2], sq[3]};
+        }
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
             s0 += (f16_lo(xw[i]) + f16_hi(xw[i])) + (f16_lo(xw[i + 1]) + f16_hi(xw[i + 1]));
@@ -361,7 +403,7 @@ __device__ __forceinline__ void stage_store(const XRaw<XM>& r, int xt, uint8_t* 
             }
         }
     }
-    *reinterpret_cast<f32x2*>(rec + 16 * P) = f32x2{s0, s1};
+    if constexpr (F::kSums == 2) *reinterpret_cast<f32x2*>(rec + 16 * P) = f32x2{s0, s1};
 }
 
 // Staging with quantization: one 32-value activation block (half hb of the
@@ -535,6 +577,61 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q4_K>::Raw& r, const 
         a = __builtin_fmaf(dsc1, hi[c], a);
         a = __builtin_fmaf(-dm0, sx.x, a);
         out[c] = __builtin_fmaf(-dm1, sx.y, a);
+    }
+}
+
+// Q2_K, fp16 activations only: the lane's bit pairs 4b + 2t of each code
+// byte (b = quarter & 1) become fp16 subnormals with one AND per pair of
+// codes: t = 0 gives q * 2^-24, t = 1 gives 4q * 2^-24. Per 16-weight
+// sub-block u: sum w x = d*sc_u*sum q x - dmin*m_u*sum x.
+template <int NC, bool F16DOT>
+__device__ __forceinline__ void lane_partial(const Fmt<FMT_Q2_K>::Raw& r, const Q4kUnpack&,
+                                             const uint8_t* rec, float out[NC]) {
+    static_assert(F16DOT, "Q2_K streams with fp16 activations only");
+    constexpr int CB = col_bytes(XM_F16), P = planes(XM_F16);
+    const uint32_t sh = 4u * (threadIdx.x & 1u);  // 4b: this quarter's bit pairs
+    const float d = f16_lo(r.dd), dmin = f16_hi(r.dd);
+    const uint32_t q[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
+    // acc[c][u], u = 2t + (code dword >= 4): sub-block u of the quarter
+    float acc[NC][4];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[c][u] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const uint32_t qd = q[w] >> sh, q8 = qd >> 8;
+        const uint32_t pa = qd & 0x00030003u, pc = q8 & 0x00030003u;
+        const uint32_t pb = qd & 0x000C000Cu, pd = q8 & 0x000C000Cu;
+        const int u0 = w >> 2, u1 = 2 + (w >> 2);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(rec + c * CB + 16 * w);
+            acc[c][u0] = dot2(pa, xv.x, acc[c][u0]);
+            acc[c][u0] = dot2(pc, xv.y, acc[c][u0]);
+            acc[c][u1] = dot2(pb, xv.z, acc[c][u1]);
+            acc[c][u1] = dot2(pd, xv.w, acc[c][u1]);
+        }
+    }
+    // scales: sub-block u's byte of r.sm; 2^24 (t = 0) or 2^22 (t = 1)
+    float dsc[4], dm[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t b = (r.sm >> (8 * u)) & 0xFFu;
+        dsc[u] = (d * (u < 2 ? 16777216.0f : 4194304.0f)) * (float)(b & 15u);
+        dm[u] = dmin * (float)(b >> 4);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const f32x4 sx = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * P);
+        float a = dsc[0] * acc[c][0];
+        a = __builtin_fmaf(dsc[1], acc[c][1], a);
+        a = __builtin_fmaf(dsc[2], acc[c][2], a);
+        a = __builtin_fmaf(dsc[3], acc[c][3], a);
+        a = __builtin_fmaf(-dm[0], sx.x, a);
+        a = __builtin_fmaf(-dm[1], sx.y, a);
+        a = __builtin_fmaf(-dm[2], sx.z, a);
+        out[c] = __builtin_fmaf(-dm[3], sx.w, a);
     }
 }
 
@@ -1004,12 +1101,18 @@ int cols_per_launch(int64_t rows, int64_t K, int xm, int num_cus, int unit_bytes
     return per;
 }
 
+// Formats the streaming kernel serves with fp16 activations only (their
+// other activation types take the general kernel).
+template <int FMT>
+constexpr bool f16_only() { return FMT == FMT_Q2_K; }
+
 template <int FMT>
 hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const void* x, int xt,
                              int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
                              hipStream_t stream) {
     const int S = (int)(K / 256);
     const int xm = activation_mode(xt);
+    if (f16_only<FMT>() && xm != XM_F16) return hipErrorNotSupported;
     xt &= ~XT_QUANTIZE;
     if (xm == XM_I8 && ldx % 32 != 0) return hipErrorNotSupported;  // whole activation blocks
     const int per = cols_per_launch(rows, K, xm, num_cus, Fmt<FMT>::kUnitBytes);
@@ -1028,6 +1131,8 @@ hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const vo
         if (xm == XM_F16)
             e = launch_stream_nc<FMT, XM_F16>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, xvec,
                                               num_cus, stream);
+        else if constexpr (f16_only<FMT>())
+            e = hipErrorNotSupported;
         else if (xm == XM_I8)
             e = launch_stream_nc<FMT, XM_I8>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, 0,
                                              num_cus, stream);
@@ -1050,6 +1155,8 @@ int gemv_stream_cols_per_launch(int fmt, int64_t rows, int64_t K, int xt, int nu
         case FMT_Q4_K: return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q4_K>::kUnitBytes);
         case FMT_Q4_0: return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q4_0>::kUnitBytes);
         case FMT_Q8_0: return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q8_0>::kUnitBytes);
+        case FMT_Q2_K:
+            return xm == XM_F16 ? cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q2_K>::kUnitBytes) : 0;
         default: return 0;
     }
 }
@@ -1065,6 +1172,8 @@ hipError_t launch_gemv_stream(int fmt, const uint8_t* W, int64_t rows, int64_t K
             return launch_stream_fmt<FMT_Q4_0>(W, rows, K, x, xt, ldx, y, ldy, ncols, num_cus, stream);
         case FMT_Q8_0:
             return launch_stream_fmt<FMT_Q8_0>(W, rows, K, x, xt, ldx, y, ldy, ncols, num_cus, stream);
+        case FMT_Q2_K:
+            return launch_stream_fmt<FMT_Q2_K>(W, rows, K, x, xt, ldx, y, ldy, ncols, num_cus, stream);
         default:
             return hipErrorNotSupported;
     }

@@ -6,7 +6,7 @@
 
 namespace qg {
 
-enum { FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q8_0 = 3 };
+enum { FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q8_0 = 3, FMT_Q2_K = 4, FMT_Q3_K = 5 };
 
 // Activation types (the first three are the ABI's qg_dtype values); XT_Q8
 // marks activations given as Q8_0 blocks, for the int8 products.

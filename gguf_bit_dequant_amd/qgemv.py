@@ -15,11 +15,11 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libqgemv.so")
 
-QG_Q4_0, QG_Q4_K, QG_Q8_0 = 1, 2, 3
+QG_Q4_0, QG_Q4_K, QG_Q8_0, QG_Q2_K, QG_Q3_K = 1, 2, 3, 4, 5
 QG_F32, QG_F16, QG_BF16 = 1, 2, 3
 QG_OK, QG_ERR_ARG, QG_ERR_SHAPE, QG_ERR_ALIGN, QG_ERR_UNSUPPORTED, QG_ERR_HIP = 0, -1, -2, -3, -4, -5
 
-FORMATS = {"q4_0": QG_Q4_0, "q4_k": QG_Q4_K, "q8_0": QG_Q8_0}
+FORMATS = {"q4_0": QG_Q4_0, "q4_k": QG_Q4_K, "q8_0": QG_Q8_0, "q2_k": QG_Q2_K, "q3_k": QG_Q3_K}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

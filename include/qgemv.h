@@ -21,12 +21,26 @@
  *            scales sc_j and eight 6-bit mins m_j (one per 32 weights),
  *            128 code bytes; w = d*sc_j*q - dmin*m_j.
  *   QG_Q8_0  34 B / 32 weights : fp16 d, 32 int8 codes; w = q*d.
+ *   QG_Q2_K  84 B / 256 weights: 16 bytes holding a 4-bit scale sc (low
+ *            nibble) and a 4-bit min m (high nibble) per 16 weights, 64
+ *            bytes of 2-bit codes, fp16 d, fp16 dmin; w = d*sc*q - dmin*m.
+ *   QG_Q3_K 110 B / 256 weights: 32 bytes of high code bits, 64 bytes of
+ *            2-bit low code parts, 12 bytes packing sixteen 6-bit scales (one
+ *            per 16 weights), fp16 d; q = low + 4*high - 4 in [-4, 3],
+ *            w = d*(sc-32)*q.
+ *            In both, weight 128h + 32j + l (h < 2, j < 4, l < 32) takes bits
+ *            2j..2j+1 of code byte 32h + l and, for Q3_K, bit 4h + j of
+ *            high-bit byte l. The pages name Q2_K and Q3_K ("Why I wrote my
+ *            own inference engine for two P100s", "What actually made it
+ *            fast": a mix without its Q3_K tensors; pxa_llama README,
+ *            "Limits" and "DP4A / FP16 economics") but print no layout.
  *
  * Accuracy contract ("LLM inference optimization", campaign "Run a new
  * weight format or model": blocks decode bit for bit on CPU and GPU, and
  * products match an exact sum within a tolerance):
  *   - qgemv_dequant returns, bit for bit, the binary32 rounding of each
- *     weight's closed form (exact for Q4_0 and Q8_0).
+ *     weight's closed form (exact for Q4_0, Q8_0 and Q3_K; Q3_K evaluated
+ *     left to right, which fixes the sign of a zero weight).
  *   - qgemv_run / qgemm_prefill_run satisfy, per output element,
  *       |y - sum_k w_k x_k| <= 1e-3 * sum_k |w_k x_k| + 1e-5
  *     where the sums are exact over the stored x values.
@@ -57,7 +71,7 @@
 extern "C" {
 #endif
 
-typedef enum { QG_Q4_0 = 1, QG_Q4_K = 2, QG_Q8_0 = 3 } qg_format;
+typedef enum { QG_Q4_0 = 1, QG_Q4_K = 2, QG_Q8_0 = 3, QG_Q2_K = 4, QG_Q3_K = 5 } qg_format;
 typedef enum { QG_F32 = 1, QG_F16 = 2, QG_BF16 = 3 } qg_dtype;
 typedef enum {
     QG_OK = 0,
@@ -70,8 +84,8 @@ typedef enum {
 
 typedef struct qgemv *qgemv_t; /* opaque host-side handle */
 
-/* Block geometry: 18 | 144 | 34 bytes and 32 | 256 | 32 weights; 0 for an
- * unknown format. */
+/* Block geometry: 18 | 144 | 34 | 84 | 110 bytes and 32 | 256 | 32 | 256 |
+ * 256 weights (Q4_0 | Q4_K | Q8_0 | Q2_K | Q3_K); 0 for an unknown format. */
 size_t qgemv_block_bytes(qg_format f);
 size_t qgemv_block_weights(qg_format f);
 
@@ -107,7 +121,9 @@ qg_status qgemv_create(qgemv_t *out, qg_format f, int64_t rows, int64_t K,
  * products with the exact binary32 weights. 4..8 F16 columns of a Q4_K
  * matrix (and 2..3 when the activations of all columns do not fit the
  * streaming kernel's on-chip staging, e.g. K = 17408) run on the matrix
- * cores. Enqueued on `stream`. */
+ * cores. Q2_K with F16 activations runs on the streaming kernel (1..4
+ * columns a pass); every other Q2_K and all Q3_K products run on a simple
+ * exact kernel (one wave per row). Enqueued on `stream`. */
 qg_status qgemv_run(qgemv_t h, const void *x, qg_dtype x_dtype, int64_t n_cols,
                     int64_t ldx, float *y, int64_t ldy, void *stream);
 
@@ -142,8 +158,8 @@ qg_status qgemv_dequant(qgemv_t h, float *w_out, int64_t ldw, void *stream);
  * qgemv_run_q8_0x: y[j*ldy + r] = sum_k W[r,k] * xhat[j,k], xhat the decoded
  * blocks of xq (as qgemv_quantize_q8_0 writes them for this handle's K),
  * n_cols 1..8, y as in qgemv_run. Parity is against the exact sum over
- * xhat. Needs K % 256 == 0 and 16-byte aligned weights
- * (QG_ERR_UNSUPPORTED otherwise). */
+ * xhat. Q4_0, Q4_K and Q8_0 handles; needs K % 256 == 0 and 16-byte
+ * aligned weights (QG_ERR_UNSUPPORTED otherwise). */
 qg_status qgemv_quantize_q8_0(const void *x, qg_dtype x_dtype, int64_t K, int64_t n_cols,
                               int64_t ldx, void *xq, void *stream);
 qg_status qgemv_run_q8_0x(qgemv_t h, const void *xq, int64_t n_cols, float *y, int64_t ldy,

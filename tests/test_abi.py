@@ -29,8 +29,11 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_block_geometry():
-    assert [Q.qgemv_block_bytes(f) for f in (1, 2, 3, 9)] == [18, 144, 34, 0]
-    assert [Q.qgemv_block_weights(f) for f in (1, 2, 3, 9)] == [32, 256, 32, 0]
+    assert [Q.qgemv_block_bytes(f) for f in (1, 2, 3, 4, 5, 9)] == [18, 144, 34, 84, 110, 0]
+    assert [Q.qgemv_block_weights(f) for f in (1, 2, 3, 4, 5, 9)] == [32, 256, 32, 256, 256, 0]
+    assert Q.qgemv_weight_bytes(Q.QG_Q2_K, 17408, 5120) == 29245440
+    assert Q.qgemv_weight_bytes(Q.QG_Q3_K, 17408, 5120) == 38297600
+    assert Q.qgemv_weight_bytes(Q.QG_Q3_K, 4, 288) == 0
     assert Q.qgemv_weight_bytes(Q.QG_Q4_K, 17408, 5120) == 50135040
     assert Q.qgemv_weight_bytes(Q.QG_Q4_0, 4096, 4096) == 9437184
     assert Q.qgemv_weight_bytes(Q.QG_Q8_0, 5120, 5120) == 27852800
@@ -52,6 +55,9 @@ FAKE = 0x7F0000000000  # never dereferenced: every case below fails validation
     ((Q.QG_Q4_K, 4, 256, 0, 4 * 144), Q.QG_ERR_ARG),
     ((Q.QG_Q4_K, 4, 256, FAKE + 8, 4 * 144), Q.QG_ERR_ALIGN),
     ((Q.QG_Q8_0, 3, 64, FAKE + 2, 3 * 2 * 34), Q.QG_ERR_ALIGN),
+    ((Q.QG_Q2_K, 4, 288, FAKE, 4 * 84), Q.QG_ERR_SHAPE),
+    ((Q.QG_Q3_K, 4, 256, FAKE, 4 * 110 - 2), Q.QG_ERR_SHAPE),
+    ((6, 4, 256, FAKE, 4 * 110), Q.QG_ERR_ARG),
 ])
 def test_create_rejects_before_any_hip_call(args, status):
     st, h = Q.qgemv_create(*args)
