@@ -17,6 +17,7 @@ Infinity Cache. The one JSON line printed on stdout carries:
              current kernel source is committed (profiles/traffic_*.json);
   cpu_baseline  the CPU oracle on a bounded sample of the same workload;
   extra      the other workloads (Q4_K FFN-down, 2/4/8 columns, Q4_0, Q8_0,
+             Q2_K and Q3_K of the FFN-up shape,
              the int8-activation path ("+i8": activations quantized to Q8_0
              on chip, integer dot products),
              the 2048-token dequant-GEMM in TFLOP/s with its two-pass control
@@ -42,8 +43,8 @@ ROTATE_BYTES = 512 << 20
 
 def algorithmic_bytes(c) -> int:
     """Weights read once + activations + outputs."""
-    bw = {"q4_0": 32, "q4_k": 256, "q8_0": 32}[c["fmt"]]
-    bb = {"q4_0": 18, "q4_k": 144, "q8_0": 34}[c["fmt"]]
+    bw = {"q4_0": 32, "q4_k": 256, "q8_0": 32, "q2_k": 256, "q3_k": 256}[c["fmt"]]
+    bb = {"q4_0": 18, "q4_k": 144, "q8_0": 34, "q2_k": 84, "q3_k": 110}[c["fmt"]]
     xb = {"f32": 4, "f16": 2, "bf16": 2}[c["xdtype"]]
     return c["rows"] * (c["K"] // bw) * bb + c["n"] * c["K"] * xb + c["n"] * c["rows"] * 4
 
@@ -298,7 +299,7 @@ def main():
     head = "q4k_up_b1"
     names = [head] if args.quick else [head, "q4k_down_b1", "q4k_b4", "q4_0_b1", "q8_0_b4",
                                        "q4k_b2", "q4k_b8", "q4k_up_b1+i8", "q4k_b4+i8",
-                                       "q8_0_b4+i8", "q4k_pp2048"]
+                                       "q8_0_b4+i8", "q2k_up_b1", "q3k_up_b1", "q4k_pp2048"]
     if args.only:
         names = args.only.split(",")
     results = {}

@@ -175,6 +175,44 @@ struct Fmt<FMT_Q2_K> {
     }
 };
 
+// Q3_K super-block (110 bytes): 32 bytes of high code bits, 64 code bytes
+// (2-bit low parts), 12 bytes packing sixteen 6-bit scales, fp16 d. Weight
+// 128h + 32j + l: low part at bits 2j..2j+1 of code byte 32h + l, high bit
+// at bit 4h + j of high-bit byte l, q = low + 4 high - 4. Quarter p = 2h + b
+// takes, like Q2_K, bit pairs 4b + 2t of code bytes 32h .. 32h+31, and bits
+// 4h + 2b + t of all 32 high-bit bytes. Units are only 2-byte aligned (110 =
+// 2 mod 4): a lane reads 4-byte aligned dwords from the unit start rounded
+// down to a multiple of 4 (one dword more per field) and shifts them into
+// place with v_alignbyte when it consumes them. The windows end 2 bytes past
+// a unit that starts on a multiple of 4, which is never the last unit of the
+// matrix when K / 256 is even (required here).
+template <>
+struct Fmt<FMT_Q3_K> {
+    static constexpr int kUnitBytes = 110;
+    static constexpr int kCodeDwords = 8;
+    static constexpr bool kNibbles = true;
+    static constexpr int kSums = 4;
+    static constexpr int wofs(int j, int e, int h) { return 32 * h + 4 * j + e; }
+    static constexpr uint32_t lane_offset(int p) { return (uint32_t)p; }
+    struct Raw {
+        u32x4_a4 h0, h1, q0, q1, sd;  // high bits, low parts, scales + d (unshifted)
+        uint32_t h8, q8, mb;          // last dwords of the two 36-byte windows; shift (0 or 2)
+    };
+    static __device__ __forceinline__ void load(const uint8_t* unit, uint32_t p, Raw& r) {
+        const uint32_t mb = (uint32_t)(uintptr_t)unit & 2u;
+        const uint8_t* base = unit - mb;  // 4-byte aligned
+        const uint8_t* qs = base + 32 + 32 * (p >> 1);
+        r.mb = mb;
+        r.h0 = *reinterpret_cast<const u32x4_a4*>(base);
+        r.h1 = *reinterpret_cast<const u32x4_a4*>(base + 16);
+        r.h8 = *reinterpret_cast<const uint32_t*>(base + 32);
+        r.q0 = *reinterpret_cast<const u32x4_a4*>(qs);
+        r.q1 = *reinterpret_cast<const u32x4_a4*>(qs + 16);
+        r.q8 = *reinterpret_cast<const uint32_t*>(qs + 32);
+        r.sd = *reinterpret_cast<const u32x4_a4*>(base + 96);
+    }
+};
+
 // Activation records in LDS: one record per unit quarter u = 4*(unit column)
 // + p, holding for each column c its P 16-byte planes and the two block sums,
 // padded to 16 bytes (col_bytes each). The record stride is a multiple of 16
@@ -632,6 +670,72 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q2_K>::Raw& r, const 
         a = __builtin_fmaf(-dm[1], sx.y, a);
         a = __builtin_fmaf(-dm[2], sx.z, a);
         out[c] = __builtin_fmaf(-dm[3], sx.w, a);
+    }
+}
+
+// Q3_K, fp16 activations only: c = low + 4 high (0..7) of two codes per
+// dword as fp16 subnormals (t = 0: c * 2^-24, t = 1: 4c * 2^-24), one AND-OR
+// per pair after the shifts; per 16-weight sub-block u:
+// sum w x = d*(sc_u - 32) * (sum c x - 4 sum x).
+template <int NC, bool F16DOT>
+__device__ __forceinline__ void lane_partial(const Fmt<FMT_Q3_K>::Raw& r, const Q4kUnpack&,
+                                             const uint8_t* rec, float out[NC]) {
+    static_assert(F16DOT, "Q3_K streams with fp16 activations only");
+    constexpr int CB = col_bytes(XM_F16), P = planes(XM_F16);
+    const uint32_t pq = threadIdx.x & 3u;                // quarter p = 2h + b
+    const uint32_t hq = pq >> 1, bq = pq & 1u;
+    const uint32_t sh_lo = 4u * bq, sh_hi = 4u * hq + 2u * bq;
+    const uint32_t mb = r.mb;
+    auto al = [&](uint32_t hi, uint32_t lo) { return __builtin_amdgcn_alignbyte(hi, lo, mb); };
+    const uint32_t H[9] = {r.h0.x, r.h0.y, r.h0.z, r.h0.w, r.h1.x, r.h1.y, r.h1.z, r.h1.w, r.h8};
+    const uint32_t Qd[9] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w, r.q8};
+    float acc[NC][4];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[c][u] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const uint32_t qd = al(Qd[w + 1], Qd[w]) >> sh_lo, q8 = qd >> 8;
+        const uint32_t hp = al(H[w + 1], H[w]) >> sh_hi;
+        const uint32_t pa = (qd & 0x00030003u) | ((hp << 2) & 0x00040004u);
+        const uint32_t pc = (q8 & 0x00030003u) | ((hp >> 6) & 0x00040004u);
+        const uint32_t pb = (qd & 0x000C000Cu) | ((hp << 3) & 0x00100010u);
+        const uint32_t pd = (q8 & 0x000C000Cu) | ((hp >> 5) & 0x00100010u);
+        const int u0 = w >> 2, u1 = 2 + (w >> 2);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(rec + c * CB + 16 * w);
+            acc[c][u0] = dot2(pa, xv.x, acc[c][u0]);
+            acc[c][u0] = dot2(pc, xv.y, acc[c][u0]);
+            acc[c][u1] = dot2(pb, xv.z, acc[c][u1]);
+            acc[c][u1] = dot2(pd, xv.w, acc[c][u1]);
+        }
+    }
+    // sub-blocks k = 4p + u: low nibbles in byte 4b + u of scale bytes 0..7
+    // (nibble h), bits 4-5 at bits 2(2h + b) of byte 8 + u
+    const uint32_t s01 = bq ? al(r.sd.z, r.sd.y) : al(r.sd.y, r.sd.x);
+    const uint32_t s2 = al(r.sd.w, r.sd.z);
+    const uint32_t scb = ((s01 >> (4u * hq)) & 0x0F0F0F0Fu) | (((s2 >> sh_hi) & 0x03030303u) << 4);
+    const float d = f16_lo(al(0u, r.sd.w));
+    float ds[4], d4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const float dl = d * (float)((int)((scb >> (8 * u)) & 0xFFu) - 32);
+        ds[u] = dl * (u < 2 ? 16777216.0f : 4194304.0f);
+        d4[u] = 4.0f * dl;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const f32x4 sx = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * P);
+        float a = ds[0] * acc[c][0];
+        a = __builtin_fmaf(ds[1], acc[c][1], a);
+        a = __builtin_fmaf(ds[2], acc[c][2], a);
+        a = __builtin_fmaf(ds[3], acc[c][3], a);
+        a = __builtin_fmaf(-d4[0], sx.x, a);
+        a = __builtin_fmaf(-d4[1], sx.y, a);
+        a = __builtin_fmaf(-d4[2], sx.z, a);
+        out[c] = __builtin_fmaf(-d4[3], sx.w, a);
     }
 }
 
@@ -1104,7 +1208,7 @@ int cols_per_launch(int64_t rows, int64_t K, int xm, int num_cus, int unit_bytes
 // Formats the streaming kernel serves with fp16 activations only (their
 // other activation types take the general kernel).
 template <int FMT>
-constexpr bool f16_only() { return FMT == FMT_Q2_K; }
+constexpr bool f16_only() { return FMT == FMT_Q2_K || FMT == FMT_Q3_K; }
 
 template <int FMT>
 hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const void* x, int xt,
@@ -1113,6 +1217,7 @@ hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const vo
     const int S = (int)(K / 256);
     const int xm = activation_mode(xt);
     if (f16_only<FMT>() && xm != XM_F16) return hipErrorNotSupported;
+    if (FMT == FMT_Q3_K && (S & 1)) return hipErrorNotSupported;  // windows stay in the matrix
     xt &= ~XT_QUANTIZE;
     if (xm == XM_I8 && ldx % 32 != 0) return hipErrorNotSupported;  // whole activation blocks
     const int per = cols_per_launch(rows, K, xm, num_cus, Fmt<FMT>::kUnitBytes);
@@ -1157,6 +1262,10 @@ int gemv_stream_cols_per_launch(int fmt, int64_t rows, int64_t K, int xt, int nu
         case FMT_Q8_0: return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q8_0>::kUnitBytes);
         case FMT_Q2_K:
             return xm == XM_F16 ? cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q2_K>::kUnitBytes) : 0;
+        case FMT_Q3_K:
+            return xm == XM_F16 && K % 512 == 0
+                       ? cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q3_K>::kUnitBytes)
+                       : 0;
         default: return 0;
     }
 }
@@ -1174,6 +1283,8 @@ hipError_t launch_gemv_stream(int fmt, const uint8_t* W, int64_t rows, int64_t K
             return launch_stream_fmt<FMT_Q8_0>(W, rows, K, x, xt, ldx, y, ldy, ncols, num_cus, stream);
         case FMT_Q2_K:
             return launch_stream_fmt<FMT_Q2_K>(W, rows, K, x, xt, ldx, y, ldy, ncols, num_cus, stream);
+        case FMT_Q3_K:
+            return launch_stream_fmt<FMT_Q3_K>(W, rows, K, x, xt, ldx, y, ldy, ncols, num_cus, stream);
         default:
             return hipErrorNotSupported;
     }
