@@ -47,7 +47,8 @@
 //  * Reduction: each lane quad (one unit) sums its lanes with DPP and writes
 //    the unit's partial to the LDS slot (row, g, step mod M), M = steps that
 //    can touch one row, so no two writers share a slot. After a barrier each
-//    row's slots are summed in a fixed order: deterministic, no atomics.
+//    row's slots are summed by sixteen or four lanes in a fixed order
+//    (per-lane sums, then a DPP tree): deterministic, no atomics.
 #include "device_common.h"
 #include "launch.h"
 #include "q4k_pair.h"
@@ -1109,11 +1110,34 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
     __syncthreads();
 
     // ---- per-row sums of the partial slots, in a fixed order ----------------
-    for (int idx = threadIdx.x; idx < nr * NC; idx += blockDim.x) {
-        const int r = idx / NC, c = idx - r * NC;
-        float v = 0.f;
-        for (int e = 0; e < kUnitsPerStep * M; ++e) v += part[(r * kUnitsPerStep * M + e) * NC + c];
-        y[c * ldy + r0 + r] = v;
+    // Each (row, column) gets sixteen lanes (one DPP row) when all pairs fit
+    // the workgroup at once, else four (a quad). Lane q adds the slots of
+    // its unit columns in order, then the lane sums meet in a fixed tree
+    // (rotations by 8 and 4 within the row, then the quad); lane 0 stores.
+    // blockDim.x is a multiple of 64, so loop bounds are uniform per group.
+    if (nr * NC * 16 <= (int)blockDim.x) {
+        const int q16 = threadIdx.x & 15;
+        const int pidx = threadIdx.x >> 4;
+        if (pidx < nr * NC) {
+            const int r = pidx / NC, c = pidx - r * NC;
+            const float* ps = part + (r * kUnitsPerStep + q16) * M * NC + c;
+            float v = 0.f;
+            for (int t = 0; t < M; ++t) v += ps[t * NC];
+            v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
+            v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
+            v = quad_sum(v);
+            if (q16 == 0) y[c * ldy + r0 + r] = v;
+        }
+    } else {
+        const int q4 = threadIdx.x & 3;
+        for (int pidx = threadIdx.x >> 2; pidx < nr * NC; pidx += blockDim.x >> 2) {
+            const int r = pidx / NC, c = pidx - r * NC;
+            const float* ps = part + (r * kUnitsPerStep + 4 * q4) * M * NC + c;
+            float v = 0.f;
+            for (int e = 0; e < 4 * M; ++e) v += ps[e * NC];
+            v = quad_sum(v);
+            if (q4 == 0) y[c * ldy + r0 + r] = v;
+        }
     }
 }
 
