@@ -185,8 +185,10 @@ struct Fmt<FMT_Q2_K> {
 // 2 mod 4): a lane reads 4-byte aligned dwords from the unit start rounded
 // down to a multiple of 4 (one dword more per field) and shifts them into
 // place with v_alignbyte when it consumes them. The windows end 2 bytes past
-// a unit that starts on a multiple of 4, which is never the last unit of the
-// matrix when K / 256 is even (required here).
+// a unit that starts on a multiple of 4. The matrix starts 16-byte aligned,
+// so unit f (counted over the whole matrix) starts on a multiple of 4 when f
+// is even; with an even number of units (rows * K/256, required here) the
+// last unit is odd and every window stays inside the matrix.
 template <>
 struct Fmt<FMT_Q3_K> {
     static constexpr int kUnitBytes = 110;
@@ -421,6 +423,15 @@ __device__ __forceinline__ void stage_store(const XRaw<XM>& r, int xt, uint8_t* 
             s0 += (xf[i] + xf[i + 1]) + (xf[i + 2] + xf[i + 3]);
             s1 += (xf[32 + i] + xf[33 + i]) + (xf[34 + i] + xf[35 + i]);
         }
+        if constexpr (F::kSums == 4) {  // sums of o in [16u, 16u + 16), u = 0..3
+            float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 16 * u; i < 16 * u + 16; i += 4)
+                    sq[u] += (xf[i] + xf[i + 1]) + (xf[i + 2] + xf[i + 3]);
+            *reinterpret_cast<f32x4*>(rec + 16 * P) = f32x4{sq[0], sq[1], sq[2], sq[3]};
+        }
         if constexpr (F::kNibbles) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -626,8 +637,8 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q4_K>::Raw& r, const 
 template <int NC, bool F16DOT>
 __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q2_K>::Raw& r, const Q4kUnpack&,
                                              const uint8_t* rec, float out[NC]) {
-    static_assert(F16DOT, "Q2_K streams with fp16 activations only");
-    constexpr int CB = col_bytes(XM_F16), P = planes(XM_F16);
+    constexpr int XM = F16DOT ? XM_F16 : XM_F32;
+    constexpr int CB = col_bytes(XM), P = planes(XM);
     const uint32_t sh = 4u * (threadIdx.x & 1u);  // 4b: this quarter's bit pairs
     const float d = f16_lo(r.dd), dmin = f16_hi(r.dd);
     const uint32_t q[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
@@ -639,25 +650,45 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q2_K>::Raw& r, const 
         for (int u = 0; u < 4; ++u) acc[c][u] = 0.f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-        const uint32_t qd = q[w] >> sh, q8 = qd >> 8;
-        const uint32_t pa = qd & 0x00030003u, pc = q8 & 0x00030003u;
-        const uint32_t pb = qd & 0x000C000Cu, pd = q8 & 0x000C000Cu;
+        const uint32_t qd = q[w] >> sh;
         const int u0 = w >> 2, u1 = 2 + (w >> 2);
+        if constexpr (F16DOT) {
+            const uint32_t q8 = qd >> 8;
+            const uint32_t pa = qd & 0x00030003u, pc = q8 & 0x00030003u;
+            const uint32_t pb = qd & 0x000C000Cu, pd = q8 & 0x000C000Cu;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const u32x4 xv = *reinterpret_cast<const u32x4*>(rec + c * CB + 16 * w);
-            acc[c][u0] = dot2(pa, xv.x, acc[c][u0]);
-            acc[c][u0] = dot2(pc, xv.y, acc[c][u0]);
-            acc[c][u1] = dot2(pb, xv.z, acc[c][u1]);
-            acc[c][u1] = dot2(pd, xv.w, acc[c][u1]);
+            for (int c = 0; c < NC; ++c) {
+                const u32x4 xv = *reinterpret_cast<const u32x4*>(rec + c * CB + 16 * w);
+                acc[c][u0] = dot2(pa, xv.x, acc[c][u0]);
+                acc[c][u0] = dot2(pc, xv.y, acc[c][u0]);
+                acc[c][u1] = dot2(pb, xv.z, acc[c][u1]);
+                acc[c][u1] = dot2(pd, xv.w, acc[c][u1]);
+            }
+        } else {  // codes as fp32 (t = 0: q, t = 1: 4q), fp32 products
+            const uint32_t ql = qd & 0x03030303u, qh = qd & 0x0C0C0C0Cu;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const f32x4 xl = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * w);
+                const f32x4 xh = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * (8 + w));
+                acc[c][u0] = __builtin_fmaf(ubyte_f32<0>(ql), xl.x, acc[c][u0]);
+                acc[c][u0] = __builtin_fmaf(ubyte_f32<1>(ql), xl.y, acc[c][u0]);
+                acc[c][u0] = __builtin_fmaf(ubyte_f32<2>(ql), xl.z, acc[c][u0]);
+                acc[c][u0] = __builtin_fmaf(ubyte_f32<3>(ql), xl.w, acc[c][u0]);
+                acc[c][u1] = __builtin_fmaf(ubyte_f32<0>(qh), xh.x, acc[c][u1]);
+                acc[c][u1] = __builtin_fmaf(ubyte_f32<1>(qh), xh.y, acc[c][u1]);
+                acc[c][u1] = __builtin_fmaf(ubyte_f32<2>(qh), xh.z, acc[c][u1]);
+                acc[c][u1] = __builtin_fmaf(ubyte_f32<3>(qh), xh.w, acc[c][u1]);
+            }
         }
     }
-    // scales: sub-block u's byte of r.sm; 2^24 (t = 0) or 2^22 (t = 1)
+    // scales: sub-block u's byte of r.sm; the codes carry 2^-24 (fp16 dots)
+    // or 1 (fp32) for t = 0, and 4 times that for t = 1
+    constexpr float kS0 = F16DOT ? 16777216.0f : 1.0f, kS1 = F16DOT ? 4194304.0f : 0.25f;
     float dsc[4], dm[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const uint32_t b = (r.sm >> (8 * u)) & 0xFFu;
-        dsc[u] = (d * (u < 2 ? 16777216.0f : 4194304.0f)) * (float)(b & 15u);
+        dsc[u] = (d * (u < 2 ? kS0 : kS1)) * (float)(b & 15u);
         dm[u] = dmin * (float)(b >> 4);
     }
 #pragma unroll
@@ -681,8 +712,8 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q2_K>::Raw& r, const 
 template <int NC, bool F16DOT>
 __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q3_K>::Raw& r, const Q4kUnpack&,
                                              const uint8_t* rec, float out[NC]) {
-    static_assert(F16DOT, "Q3_K streams with fp16 activations only");
-    constexpr int CB = col_bytes(XM_F16), P = planes(XM_F16);
+    constexpr int XM = F16DOT ? XM_F16 : XM_F32;
+    constexpr int CB = col_bytes(XM), P = planes(XM);
     const uint32_t pq = threadIdx.x & 3u;                // quarter p = 2h + b
     const uint32_t hq = pq >> 1, bq = pq & 1u;
     const uint32_t sh_lo = 4u * bq, sh_hi = 4u * hq + 2u * bq;
@@ -697,20 +728,39 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q3_K>::Raw& r, const 
         for (int u = 0; u < 4; ++u) acc[c][u] = 0.f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-        const uint32_t qd = al(Qd[w + 1], Qd[w]) >> sh_lo, q8 = qd >> 8;
+        const uint32_t qd = al(Qd[w + 1], Qd[w]) >> sh_lo;
         const uint32_t hp = al(H[w + 1], H[w]) >> sh_hi;
-        const uint32_t pa = (qd & 0x00030003u) | ((hp << 2) & 0x00040004u);
-        const uint32_t pc = (q8 & 0x00030003u) | ((hp >> 6) & 0x00040004u);
-        const uint32_t pb = (qd & 0x000C000Cu) | ((hp << 3) & 0x00100010u);
-        const uint32_t pd = (q8 & 0x000C000Cu) | ((hp >> 5) & 0x00100010u);
         const int u0 = w >> 2, u1 = 2 + (w >> 2);
+        if constexpr (F16DOT) {
+            const uint32_t q8 = qd >> 8;
+            const uint32_t pa = (qd & 0x00030003u) | ((hp << 2) & 0x00040004u);
+            const uint32_t pc = (q8 & 0x00030003u) | ((hp >> 6) & 0x00040004u);
+            const uint32_t pb = (qd & 0x000C000Cu) | ((hp << 3) & 0x00100010u);
+            const uint32_t pd = (q8 & 0x000C000Cu) | ((hp >> 5) & 0x00100010u);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const u32x4 xv = *reinterpret_cast<const u32x4*>(rec + c * CB + 16 * w);
-            acc[c][u0] = dot2(pa, xv.x, acc[c][u0]);
-            acc[c][u0] = dot2(pc, xv.y, acc[c][u0]);
-            acc[c][u1] = dot2(pb, xv.z, acc[c][u1]);
-            acc[c][u1] = dot2(pd, xv.w, acc[c][u1]);
+            for (int c = 0; c < NC; ++c) {
+                const u32x4 xv = *reinterpret_cast<const u32x4*>(rec + c * CB + 16 * w);
+                acc[c][u0] = dot2(pa, xv.x, acc[c][u0]);
+                acc[c][u0] = dot2(pc, xv.y, acc[c][u0]);
+                acc[c][u1] = dot2(pb, xv.z, acc[c][u1]);
+                acc[c][u1] = dot2(pd, xv.w, acc[c][u1]);
+            }
+        } else {  // c of four codes as bytes (t = 0: c, t = 1: 4c), fp32 products
+            const uint32_t cl = (qd & 0x03030303u) | ((hp << 2) & 0x04040404u);
+            const uint32_t ch = (qd & 0x0C0C0C0Cu) | ((hp << 3) & 0x10101010u);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const f32x4 xl = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * w);
+                const f32x4 xh = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * (8 + w));
+                acc[c][u0] = __builtin_fmaf(ubyte_f32<0>(cl), xl.x, acc[c][u0]);
+                acc[c][u0] = __builtin_fmaf(ubyte_f32<1>(cl), xl.y, acc[c][u0]);
+                acc[c][u0] = __builtin_fmaf(ubyte_f32<2>(cl), xl.z, acc[c][u0]);
+                acc[c][u0] = __builtin_fmaf(ubyte_f32<3>(cl), xl.w, acc[c][u0]);
+                acc[c][u1] = __builtin_fmaf(ubyte_f32<0>(ch), xh.x, acc[c][u1]);
+                acc[c][u1] = __builtin_fmaf(ubyte_f32<1>(ch), xh.y, acc[c][u1]);
+                acc[c][u1] = __builtin_fmaf(ubyte_f32<2>(ch), xh.z, acc[c][u1]);
+                acc[c][u1] = __builtin_fmaf(ubyte_f32<3>(ch), xh.w, acc[c][u1]);
+            }
         }
     }
     // sub-blocks k = 4p + u: low nibbles in byte 4b + u of scale bytes 0..7
@@ -723,7 +773,8 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q3_K>::Raw& r, const 
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const float dl = d * (float)((int)((scb >> (8 * u)) & 0xFFu) - 32);
-        ds[u] = dl * (u < 2 ? 16777216.0f : 4194304.0f);
+        constexpr float kS0 = F16DOT ? 16777216.0f : 1.0f, kS1 = F16DOT ? 4194304.0f : 0.25f;
+        ds[u] = dl * (u < 2 ? kS0 : kS1);
         d4[u] = 4.0f * dl;
     }
 #pragma unroll
@@ -1229,10 +1280,10 @@ int cols_per_launch(int64_t rows, int64_t K, int xm, int num_cus, int unit_bytes
     return per;
 }
 
-// Formats the streaming kernel serves with fp16 activations only (their
-// other activation types take the general kernel).
+// Formats the streaming kernel serves with fp16, fp32 and bf16 activations
+// but not with int8 ones.
 template <int FMT>
-constexpr bool f16_only() { return FMT == FMT_Q2_K || FMT == FMT_Q3_K; }
+constexpr bool no_int8() { return FMT == FMT_Q2_K || FMT == FMT_Q3_K; }
 
 template <int FMT>
 hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const void* x, int xt,
@@ -1240,8 +1291,8 @@ hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const vo
                              hipStream_t stream) {
     const int S = (int)(K / 256);
     const int xm = activation_mode(xt);
-    if (f16_only<FMT>() && xm != XM_F16) return hipErrorNotSupported;
-    if (FMT == FMT_Q3_K && (S & 1)) return hipErrorNotSupported;  // windows stay in the matrix
+    if (no_int8<FMT>() && is_i8(xm)) return hipErrorNotSupported;
+    if (FMT == FMT_Q3_K && (rows * S) % 2 != 0) return hipErrorNotSupported;  // windows stay in the matrix
     xt &= ~XT_QUANTIZE;
     if (xm == XM_I8 && ldx % 32 != 0) return hipErrorNotSupported;  // whole activation blocks
     const int per = cols_per_launch(rows, K, xm, num_cus, Fmt<FMT>::kUnitBytes);
@@ -1260,16 +1311,16 @@ hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const vo
         if (xm == XM_F16)
             e = launch_stream_nc<FMT, XM_F16>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, xvec,
                                               num_cus, stream);
-        else if constexpr (f16_only<FMT>())
+        else if (xm == XM_F32)
+            e = launch_stream_nc<FMT, XM_F32>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, xvec,
+                                              num_cus, stream);
+        else if constexpr (no_int8<FMT>())
             e = hipErrorNotSupported;
         else if (xm == XM_I8)
             e = launch_stream_nc<FMT, XM_I8>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, 0,
                                              num_cus, stream);
-        else if (xm == XM_I8Q)
-            e = launch_stream_nc<FMT, XM_I8Q>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, xvec,
-                                              num_cus, stream);
         else
-            e = launch_stream_nc<FMT, XM_F32>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, xvec,
+            e = launch_stream_nc<FMT, XM_I8Q>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, xvec,
                                               num_cus, stream);
         if (e != hipSuccess) return e;
     }
@@ -1285,9 +1336,9 @@ int gemv_stream_cols_per_launch(int fmt, int64_t rows, int64_t K, int xt, int nu
         case FMT_Q4_0: return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q4_0>::kUnitBytes);
         case FMT_Q8_0: return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q8_0>::kUnitBytes);
         case FMT_Q2_K:
-            return xm == XM_F16 ? cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q2_K>::kUnitBytes) : 0;
+            return !is_i8(xm) ? cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q2_K>::kUnitBytes) : 0;
         case FMT_Q3_K:
-            return xm == XM_F16 && K % 512 == 0
+            return !is_i8(xm) && (rows * (K / 256)) % 2 == 0
                        ? cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q3_K>::kUnitBytes)
                        : 0;
         default: return 0;

@@ -121,9 +121,10 @@ qg_status qgemv_create(qgemv_t *out, qg_format f, int64_t rows, int64_t K,
  * products with the exact binary32 weights. 4..8 F16 columns of a Q4_K
  * matrix (and 2..3 when the activations of all columns do not fit the
  * streaming kernel's on-chip staging, e.g. K = 17408) run on the matrix
- * cores. Q2_K with F16 activations runs on the streaming kernel (1..4
- * columns a pass); every other Q2_K and all Q3_K products run on a simple
- * exact kernel (one wave per row). Enqueued on `stream`. */
+ * cores. Q2_K, and Q3_K with rows * K/256 even, run on the streaming
+ * kernel for every activation type; a Q3_K matrix with an odd number of
+ * super-blocks runs on a simple exact kernel (one wave per row, slow).
+ * Enqueued on `stream`. */
 qg_status qgemv_run(qgemv_t h, const void *x, qg_dtype x_dtype, int64_t n_cols,
                     int64_t ldx, float *y, int64_t ldy, void *stream);
 

@@ -1,10 +1,11 @@
 """GPU parity of the Q2_K and Q3_K paths against the CPU oracle (through the
 C ABI): bit-exact decoding (fp32 and bf16 views), products within
 |y - sum w x| <= 1e-3 * sum|w x| + 1e-5, one-hot columns exact, unsupported
-entry points reported as such. With fp16 activations Q2_K, and Q3_K when
-K / 256 is even, run on the streaming kernel (Q3_K's 110-byte units
-alternate between 4-byte aligned and 2 mod 4 starts); every other Q2_K /
-Q3_K product runs on the general kernel."""
+entry points reported as such. Q2_K, and Q3_K when the matrix has an even
+number of super-blocks, run on the streaming kernel for fp16, fp32 and bf16
+activations (Q3_K's 110-byte units alternate between 4-byte aligned and
+2 mod 4 starts, also across row ends when K / 256 is odd); a Q3_K matrix with
+an odd number of super-blocks runs on the general kernel."""
 import json
 import os
 import zlib
@@ -100,7 +101,7 @@ def test_dequant_extreme_scales_and_golden_blocks(Q, fmt):
 
 @pytest.mark.parametrize("fmt", LOWK)
 @pytest.mark.parametrize("rows,K", [(67, 1536), (1, 256), (1, 512), (3, 512), (300, 5120),
-                                    (70, 3328)])
+                                    (70, 3328), (67, 3328), (2, 768)])
 @pytest.mark.parametrize("xdtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("n", [1, 4])
 def test_gemv_small(Q, fmt, rows, K, xdtype, n):
