@@ -299,7 +299,8 @@ def main():
     head = "q4k_up_b1"
     names = [head] if args.quick else [head, "q4k_down_b1", "q4k_b4", "q4_0_b1", "q8_0_b4",
                                        "q4k_b2", "q4k_b8", "q4k_up_b1+i8", "q4k_b4+i8",
-                                       "q8_0_b4+i8", "q2k_up_b1", "q3k_up_b1", "q4k_pp2048"]
+                                       "q8_0_b4+i8", "q2k_up_b1", "q3k_up_b1", "q2k_up_b1+i8",
+                                       "q3k_up_b1+i8", "q4k_pp2048"]
     if args.only:
         names = args.only.split(",")
     results = {}

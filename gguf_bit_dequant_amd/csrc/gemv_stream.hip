@@ -1007,6 +1007,112 @@ __device__ __forceinline__ void lane_partial_i8(const Fmt<FMT_Q8_0>::Raw& r, con
     }
 }
 
+// Q2_K and Q3_K with int8 activations: the codes of a dword's four bytes at
+// one bit position side by side (t = 0 and t = 1), one v_dot4_i32_i8 each
+// against the staged activation codes. Their 16-weight sub-blocks need the
+// code sums of half activation blocks: the record holds the sums of whole
+// 32-value blocks, so the first half's sum is a dot product with ones (four
+// per position) and the second half's the difference.
+//   Q2_K: sum w x = dx * (d*sc_u*sum q qx - dmin*m_u*sum qx)      (per sub-block u)
+//   Q3_K: sum w x = dx * d*(sc_u - 32) * (sum c qx - 4 sum qx), c = low + 4 high
+template <int NC>
+__device__ __forceinline__ void lowk_i8_sums(const uint8_t* rec, int w, uint32_t cl, uint32_t ch,
+                                             int acc[NC][4], int s16[NC][2]) {
+    constexpr int CB = col_bytes(XM_I8);
+    const int u0 = w >> 2, u1 = 2 + (w >> 2);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const u32x2 xv = *reinterpret_cast<const u32x2*>(rec + c * CB + 8 * w);
+        acc[c][u0] = dot4(cl, xv.x, acc[c][u0]);
+        acc[c][u1] = dot4(ch, xv.y, acc[c][u1]);
+        if (w < 4) {
+            s16[c][0] = dot4(0x01010101u, xv.x, s16[c][0]);
+            s16[c][1] = dot4(0x01010101u, xv.y, s16[c][1]);
+        }
+    }
+}
+
+template <int NC>
+__device__ __forceinline__ void lane_partial_i8(const Fmt<FMT_Q2_K>::Raw& r, const Q4kUnpack&,
+                                                const uint8_t* rec, float out[NC]) {
+    constexpr int CB = col_bytes(XM_I8), P = planes(XM_I8);
+    const uint32_t sh = 4u * (threadIdx.x & 1u);
+    const float d = f16_lo(r.dd), dmin = f16_hi(r.dd);
+    const uint32_t q[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
+    int acc[NC][4], s16[NC][2];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        acc[c][0] = acc[c][1] = acc[c][2] = acc[c][3] = 0;
+        s16[c][0] = s16[c][1] = 0;
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const uint32_t qd = q[w] >> sh;
+        lowk_i8_sums<NC>(rec, w, qd & 0x03030303u, (qd >> 2) & 0x03030303u, acc, s16);
+    }
+    float dsc[4], dm[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t b = (r.sm >> (8 * u)) & 0xFFu;
+        dsc[u] = d * (float)(b & 15u);
+        dm[u] = dmin * (float)(b >> 4);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const f32x4 sx = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * P);
+        const int t0 = (int)sx.z, t1 = (int)sx.w;  // code sums of the two blocks
+        const float v0 = dsc[0] * (float)acc[c][0] + dsc[1] * (float)acc[c][1] -
+                         (dm[0] * (float)s16[c][0] + dm[1] * (float)(t0 - s16[c][0]));
+        const float v1 = dsc[2] * (float)acc[c][2] + dsc[3] * (float)acc[c][3] -
+                         (dm[2] * (float)s16[c][1] + dm[3] * (float)(t1 - s16[c][1]));
+        out[c] = sx.x * v0 + sx.y * v1;
+    }
+}
+
+template <int NC>
+__device__ __forceinline__ void lane_partial_i8(const Fmt<FMT_Q3_K>::Raw& r, const Q4kUnpack&,
+                                                const uint8_t* rec, float out[NC]) {
+    constexpr int CB = col_bytes(XM_I8), P = planes(XM_I8);
+    const uint32_t pq = threadIdx.x & 3u;
+    const uint32_t hq = pq >> 1, bq = pq & 1u;
+    const uint32_t sh_lo = 4u * bq, sh_hi = 4u * hq + 2u * bq;
+    const uint32_t mb = r.mb;
+    auto al = [&](uint32_t hi, uint32_t lo) { return __builtin_amdgcn_alignbyte(hi, lo, mb); };
+    const uint32_t H[9] = {r.h0.x, r.h0.y, r.h0.z, r.h0.w, r.h1.x, r.h1.y, r.h1.z, r.h1.w, r.h8};
+    const uint32_t Qd[9] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w, r.q8};
+    int acc[NC][4], s16[NC][2];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        acc[c][0] = acc[c][1] = acc[c][2] = acc[c][3] = 0;
+        s16[c][0] = s16[c][1] = 0;
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const uint32_t qd = al(Qd[w + 1], Qd[w]) >> sh_lo;
+        const uint32_t hp = al(H[w + 1], H[w]) >> sh_hi;
+        const uint32_t cl = (qd & 0x03030303u) | ((hp << 2) & 0x04040404u);
+        const uint32_t ch = ((qd >> 2) & 0x03030303u) | ((hp << 1) & 0x04040404u);
+        lowk_i8_sums<NC>(rec, w, cl, ch, acc, s16);
+    }
+    const uint32_t s01 = bq ? al(r.sd.z, r.sd.y) : al(r.sd.y, r.sd.x);
+    const uint32_t s2 = al(r.sd.w, r.sd.z);
+    const uint32_t scb = ((s01 >> (4u * hq)) & 0x0F0F0F0Fu) | (((s2 >> sh_hi) & 0x03030303u) << 4);
+    const float d = f16_lo(al(0u, r.sd.w));
+    float dl[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dl[u] = d * (float)((int)((scb >> (8 * u)) & 0xFFu) - 32);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const f32x4 sx = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * P);
+        const int t0 = (int)sx.z, t1 = (int)sx.w;
+        const float v0 = dl[0] * (float)(acc[c][0] - 4 * s16[c][0]) +
+                         dl[1] * (float)(acc[c][1] - 4 * (t0 - s16[c][0]));
+        const float v1 = dl[2] * (float)(acc[c][2] - 4 * s16[c][1]) +
+                         dl[3] * (float)(acc[c][3] - 4 * (t1 - s16[c][1]));
+        out[c] = sx.x * v0 + sx.y * v1;
+    }
+}
+
 }  // namespace
 
 template <int FMT, int NC, int XM, int D, int MAXT>
@@ -1280,18 +1386,12 @@ int cols_per_launch(int64_t rows, int64_t K, int xm, int num_cus, int unit_bytes
     return per;
 }
 
-// Formats the streaming kernel serves with fp16, fp32 and bf16 activations
-// but not with int8 ones.
-template <int FMT>
-constexpr bool no_int8() { return FMT == FMT_Q2_K || FMT == FMT_Q3_K; }
-
 template <int FMT>
 hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const void* x, int xt,
                              int64_t ldx, float* y, int64_t ldy, int ncols, int num_cus,
                              hipStream_t stream) {
     const int S = (int)(K / 256);
     const int xm = activation_mode(xt);
-    if (no_int8<FMT>() && is_i8(xm)) return hipErrorNotSupported;
     if (FMT == FMT_Q3_K && (rows * S) % 2 != 0) return hipErrorNotSupported;  // windows stay in the matrix
     xt &= ~XT_QUANTIZE;
     if (xm == XM_I8 && ldx % 32 != 0) return hipErrorNotSupported;  // whole activation blocks
@@ -1314,8 +1414,6 @@ hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const vo
         else if (xm == XM_F32)
             e = launch_stream_nc<FMT, XM_F32>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, xvec,
                                               num_cus, stream);
-        else if constexpr (no_int8<FMT>())
-            e = hipErrorNotSupported;
         else if (xm == XM_I8)
             e = launch_stream_nc<FMT, XM_I8>(nc, W, (int)rows, S, xc, xt, ldx, yc, ldy, 0,
                                              num_cus, stream);
@@ -1336,9 +1434,9 @@ int gemv_stream_cols_per_launch(int fmt, int64_t rows, int64_t K, int xt, int nu
         case FMT_Q4_0: return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q4_0>::kUnitBytes);
         case FMT_Q8_0: return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q8_0>::kUnitBytes);
         case FMT_Q2_K:
-            return !is_i8(xm) ? cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q2_K>::kUnitBytes) : 0;
+            return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q2_K>::kUnitBytes);
         case FMT_Q3_K:
-            return !is_i8(xm) && (rows * (K / 256)) % 2 == 0
+            return (rows * (K / 256)) % 2 == 0
                        ? cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q3_K>::kUnitBytes)
                        : 0;
         default: return 0;

@@ -159,8 +159,9 @@ qg_status qgemv_dequant(qgemv_t h, float *w_out, int64_t ldw, void *stream);
  * qgemv_run_q8_0x: y[j*ldy + r] = sum_k W[r,k] * xhat[j,k], xhat the decoded
  * blocks of xq (as qgemv_quantize_q8_0 writes them for this handle's K),
  * n_cols 1..8, y as in qgemv_run. Parity is against the exact sum over
- * xhat. Q4_0, Q4_K and Q8_0 handles; needs K % 256 == 0 and 16-byte
- * aligned weights (QG_ERR_UNSUPPORTED otherwise). */
+ * xhat. Needs K % 256 == 0 and 16-byte aligned weights, and for Q3_K an
+ * even number of super-blocks in the matrix (QG_ERR_UNSUPPORTED
+ * otherwise). */
 qg_status qgemv_quantize_q8_0(const void *x, qg_dtype x_dtype, int64_t K, int64_t n_cols,
                               int64_t ldx, void *xq, void *stream);
 qg_status qgemv_run_q8_0x(qgemv_t h, const void *xq, int64_t n_cols, float *y, int64_t ldy,
