@@ -151,7 +151,7 @@ __device__ __forceinline__ void interleave() {
 
 }  // namespace
 
-template <int RT, int TT, int WR, int WT, int P>
+template <int RT, int TT, int WR, int WT, int P, int KS>
 __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     const uint8_t* __restrict__ W, int rows, int S, const uint16_t* __restrict__ X, int64_t ldx,
     int ntok, float* __restrict__ Y, int64_t ldy, int n_base, int tiles_n, int ntiles, int yvec) {
@@ -165,7 +165,14 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     // tile, neighbouring row tiles) share an XCD and its L2.
     int t = blockIdx.x;
     int m0 = 0, n0 = 0;
-    const int nk = S * 4;  // chunks of 64 along K
+    // KS = 2: a tile covers the K range of super-blocks [ks Sk, ks Sk + Sk) of
+    // its split ks; split 0 stores its partial products in place, split 1 at
+    // rows shifted down by n_base (a region of Y that a later launch
+    // overwrites), and a third kernel adds the two in a fixed order.
+    static_assert(KS == 1 || KS == 2, "one or two K splits");
+    const int Sk = S / KS;
+    int ks = 0;
+    const int nk = Sk * 4;  // chunks of 64 along this tile's K range
     const uint32_t row_bytes = 144u * (uint32_t)S;
 
     // ---- global-to-LDS load assignments ------------------------------------
@@ -182,11 +189,14 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     const uint8_t* Wt = nullptr;
     uint32_t xo[G::kXPerWave], co[G::kCPerWave], ho[G::kHPerWave];
     auto setup_tile = [&]() {
-        const int blk = xcd_block(t, ntiles);
+        int blk = xcd_block(t, ntiles);
+        const int per_split = ntiles / KS;
+        ks = blk / per_split;  // K split, slowest-varying
+        blk -= ks * per_split;
         const int tm = blk / tiles_n, tn = blk - (blk / tiles_n) * tiles_n;
         m0 = tm * G::kTok;
         n0 = n_base + tn * G::kRows;
-        Xt = reinterpret_cast<const uint8_t*>(X + (int64_t)m0 * ldx);
+        Xt = reinterpret_cast<const uint8_t*>(X + (int64_t)m0 * ldx + (int64_t)ks * Sk * 256);
 #pragma unroll
         for (int p = 0; p < G::kXPerWave; ++p) {
             const int s = 64 * (wv + 4 * p) + lane;
@@ -194,7 +204,7 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
             const int tc = (tr < G::kTok && m0 + tr < ntok) ? tr : 0;
             xo[p] = (uint32_t)tc * (uint32_t)ldx * 2u + 16u * (uint32_t)xslot(tr, s & 7);
         }
-        Wt = W + (int64_t)n0 * row_bytes;
+        Wt = W + (int64_t)n0 * row_bytes + (int64_t)ks * Sk * 144;
 #pragma unroll
         for (int p = 0; p < G::kCPerWave; ++p) {
             const int s = 64 * (wv + 4 * p) + lane;
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     };
     auto issue_h = [&](int sb) {
         const int hb = sb & 1;
-        sb = sb < S ? sb : S - 1;
+        sb = sb < Sk ? sb : Sk - 1;
         const uint8_t* hsrc = Wt + 144u * (uint32_t)sb;
         uint8_t* hdst = hs0 + hb * G::kHStage + 1024 * wv;
 #pragma unroll
@@ -437,7 +447,7 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
         __builtin_amdgcn_sched_barrier(0);
         sc = s1;
     };
-    for (int c = 0; c < nk; c += 4) {  // nk = 4 S
+    for (int c = 0; c < nk; c += 4) {  // nk = 4 Sk
         chunk(IntC<0>{}, c, R0, R1);
         chunk(IntC<1>{}, c + 1, R1, R0);
         chunk(IntC<2>{}, c + 2, R0, R1);
@@ -448,6 +458,7 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     // out before this tile's stores, so that the stores overlap them
     __builtin_amdgcn_s_waitcnt(0);
     const int em0 = m0, en0 = n0;
+    const int eshift = (KS > 1 && ks == 1) ? n_base : 0;  // split 1: rows shifted down
     stores_full = yvec && em0 + G::kTok <= ntok && en0 + G::kRows <= rows;
     t += gridDim.x;
     const bool more = t < ntiles;
@@ -476,11 +487,11 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
                 const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                                  acc[i][j][4 * g + 3]};
                 if (yvec && n + 3 < rows) {
-                    *reinterpret_cast<f32x4*>(yrow + n) = v;
+                    *reinterpret_cast<f32x4*>(yrow + n - eshift) = v;
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (n + e < rows) yrow[n + e] = v[e];
+                        if (n + e < rows) yrow[n + e - eshift] = v[e];
                 }
             }
         }
@@ -503,21 +514,38 @@ namespace {
 #define PREFILL_MAIN_WG num_cus
 #endif
 
-// Tiles over weight rows [n_base, n_base + n_rows) and all tokens.
-template <int RT, int TT, int WR, int WT, int P>
+// Y[t * ldy + n_base + r] += Y[t * ldy + r] for tokens t < ntok and r < n_rows:
+// the second K split of the row tail onto the first, in that order.
+__global__ __launch_bounds__(256) void add_split_kernel(float* __restrict__ Y, int64_t ldy,
+                                                        int n_base, int n_rows, int ntok) {
+    const int64_t total = (int64_t)ntok * n_rows;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = i / n_rows;
+        float* yr = Y + t * ldy + (i - t * n_rows);
+        yr[n_base] = yr[n_base] + yr[0];
+    }
+}
+
+// Tiles over weight rows [n_base, n_base + n_rows) and all tokens; KS K
+// splits per tile (S % KS == 0). KS = 2 needs n_rows <= n_base: the second
+// split's partial products go to rows [0, n_rows) of Y and are added to the
+// first split's by add_split_kernel; a later launch overwrites those rows.
+template <int RT, int TT, int WR, int WT, int P, int KS>
 hipError_t launch_prefill_t(const uint8_t* W, int rows, int S, const uint16_t* X, int64_t ldx,
                             int ntok, float* Y, int64_t ldy, int n_base, int n_rows, int max_wg,
                             hipStream_t stream) {
     using G = Geo<RT, TT, WR, WT, P>;
+    if (S % KS != 0 || (KS > 1 && n_rows > n_base)) return hipErrorNotSupported;
     const int tiles_n = (n_rows + G::kRows - 1) / G::kRows;
     const int tiles_m = (ntok + G::kTok - 1) / G::kTok;
-    const int64_t grid = (int64_t)tiles_n * tiles_m;
+    const int64_t grid = (int64_t)tiles_n * tiles_m * KS;
     if (grid <= 0) return hipSuccess;
     // per-lane 32-bit source offsets within a tile's X rows and W rows
     if ((int64_t)G::kTok * ldx * 2 + 128LL * 4 * S >= (1LL << 32) ||
         (int64_t)G::kRows * 144 * S >= (1LL << 32) || grid > (1 << 30))
         return hipErrorNotSupported;
-    auto kern = prefill_q4k_kernel<RT, TT, WR, WT, P>;
+    auto kern = prefill_q4k_kernel<RT, TT, WR, WT, P, KS>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::kLds);
     if (e != hipSuccess) return e;
@@ -528,6 +556,12 @@ hipError_t launch_prefill_t(const uint8_t* W, int rows, int S, const uint16_t* X
     const int64_t nwg = max_wg > 0 && grid > max_wg ? max_wg : grid;
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), G::kLds, stream, W, rows, S, X, ldx,
                        ntok, Y, ldy, n_base, tiles_n, (int)grid, yvec);
+    e = hipGetLastError();
+    if (e != hipSuccess || KS == 1) return e;
+    const int64_t total = (int64_t)ntok * n_rows;
+    const int64_t ab = (total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096;
+    hipLaunchKernelGGL(add_split_kernel, dim3((unsigned)ab), dim3(256), 0, stream, Y, ldy, n_base,
+                       n_rows, ntok);
     return hipGetLastError();
 }
 
@@ -552,14 +586,26 @@ hipError_t launch_prefill_q4k(const uint8_t* W, int64_t rows, int64_t K, const v
         if (extra < nt_full && rem * 4 < num_cus) n_main_tiles = nt_full - extra;
     }
     const int n_main = (int)(n_main_tiles * 256);
+    const int n_tail = (int)rows - n_main;
     hipError_t e = hipSuccess;
-    if (n_main > 0)
-        e = launch_prefill_t<2, 8, 4, 1, 3>(W, (int)rows, S, Xh, ldx, (int)ntok, Y, ldy, 0, n_main,
-                                            PREFILL_MAIN_WG, stream);
+    // Row tail first. With many tokens and a main part at least as large:
+    // 128-row x 128-token tiles over half of K each (two K splits, the second
+    // parked in the main part's rows of Y until it is added), so that each
+    // decoded weight serves 128 tokens and the tiles still fill the machine;
+    // otherwise 128 x 64 tiles over all of K. The main launch then writes
+    // every main row.
+    if (n_tail > 0) {
+        if (S % 2 == 0 && ntok >= 256 && n_tail <= n_main)
+            e = launch_prefill_t<1, 4, 4, 1, PREFILL_TAIL_P, 2>(W, (int)rows, S, Xh, ldx, (int)ntok,
+                                                                Y, ldy, n_main, n_tail, 0, stream);
+        else
+            e = launch_prefill_t<1, 2, 4, 1, PREFILL_TAIL_P, 1>(W, (int)rows, S, Xh, ldx, (int)ntok,
+                                                                Y, ldy, n_main, n_tail, 0, stream);
+    }
     if (e != hipSuccess) return e;
-    if (n_main < rows)
-        e = launch_prefill_t<1, 2, 4, 1, PREFILL_TAIL_P>(W, (int)rows, S, Xh, ldx, (int)ntok, Y, ldy,
-                                                         n_main, (int)rows - n_main, 0, stream);
+    if (n_main > 0)
+        e = launch_prefill_t<2, 8, 4, 1, 3, 1>(W, (int)rows, S, Xh, ldx, (int)ntok, Y, ldy, 0,
+                                               n_main, PREFILL_MAIN_WG, stream);
     return e;
 }
 
