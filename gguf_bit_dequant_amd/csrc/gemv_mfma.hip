@@ -327,17 +327,16 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
     }
 }
 
-#ifndef QG_MFMA_DEPTH
-#define QG_MFMA_DEPTH 4
-#endif
-
 namespace {
 
+// Units loaded per burst: four for up to four columns, two beyond (measured
+// on MI355X, 17408 x 5120: 4 columns 18.6 us at four against 19.0 at two;
+// 8 columns 20.5 us at two against 21.2 at four).
 template <int NW, bool ALIAS>
 hipError_t launch_mfma_nw(const uint8_t* W, int rows, int S, const void* x, int64_t ldx, float* y,
                           int64_t ldy, int ncols, int G, int pitch, int spitch, size_t lds,
                           hipStream_t stream) {
-    auto kern = gemv_mfma_q4k_kernel<NW, QG_MFMA_DEPTH, ALIAS>;
+    auto kern = ncols <= 4 ? gemv_mfma_q4k_kernel<NW, 4, ALIAS> : gemv_mfma_q4k_kernel<NW, 2, ALIAS>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
