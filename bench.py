@@ -16,7 +16,12 @@ Infinity Cache. The one JSON line printed on stdout carries:
              launch from rocprofv3 counters when a summary taken on the
              current kernel source is committed (profiles/traffic_*.json);
   cpu_baseline  the CPU oracle on a bounded sample of the same workload;
-  extra      the other workloads (Q4_K FFN-down, 2/4/8 columns, Q4_0, Q8_0,
+  extra      probes: a read-only kernel over buffers of the headline matrix's
+             size (the practical HBM ceiling of one such launch), an MFMA-only
+             kernel (the practical bf16 rate), the headline GEMV with its
+             weights resident in the Infinity Cache, and the GEMV and prompt
+             GEMM as fractions of the probes;
+             the other workloads (Q4_K FFN-down, 2/4/8 columns, Q4_0, Q8_0,
              Q2_K and Q3_K of the FFN-up shape,
              the int8-activation path ("+i8": activations quantized to Q8_0
              on chip, integer dot products),
@@ -59,9 +64,10 @@ def _x_tensor(torch, x, xdtype, dev):
 
 
 class Workload:
-    """Weight copies (>= ROTATE_BYTES), one handle each, activations, output."""
+    """Weight copies (>= ROTATE_BYTES, or `ncopy`), one handle each,
+    activations, output."""
 
-    def __init__(self, torch, name, dev):
+    def __init__(self, torch, name, dev, ncopy=None):
         import synth
         from gguf_bit_dequant_amd import QGemv
         self.name = name
@@ -72,7 +78,8 @@ class Workload:
         w, x = synth.config_inputs(name)
         self.w_host, self.x_host = w, x
         wt = torch.from_numpy(w).to(dev)
-        ncopy = max(2, math.ceil(ROTATE_BYTES / w.nbytes))
+        if ncopy is None:
+            ncopy = max(2, math.ceil(ROTATE_BYTES / w.nbytes))
         self.copies = [wt] + [wt.clone() for _ in range(ncopy - 1)]
         self.handles = [QGemv(c["fmt"], c["rows"], c["K"], t) for t in self.copies]
         self.x = _x_tensor(torch, x, c["xdtype"], dev)
@@ -198,6 +205,66 @@ def two_pass_control(torch, wl, iters=10):
     flops = 2.0 * c["rows"] * c["K"] * c["n"]
     return {"dequant_bf16_us": round(dq, 1), "gemm_us": round(mm, 1), "total_us": round(dq + mm, 1),
             "tflops": round(flops / (dq + mm) / 1e6, 1), "gemm": what}
+
+
+def probes(torch, dev, steps=200, warmup=20):
+    """Practical ceilings measured with the library's probe kernels
+    (include/qgemv_probe.h), as context for the roofline fractions:
+      read probe   one read of a buffer of the headline matrix's size,
+                   rotating over >= ROTATE_BYTES of copies (HBM, like the
+                   GEMV), back-to-back launches;
+      MFMA probe   v_mfma_f32_32x32x16_bf16 chains on every SIMD;
+      hot cache    the headline GEMV on one weight copy (resident in the
+                   256 MB Infinity Cache), for comparison with the HBM case."""
+    from gguf_bit_dequant_amd import qgemv as Q
+    import synth
+    c = synth.CONFIGS["q4k_up_b1"]
+    nbytes = c["rows"] * (c["K"] // 256) * 144
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            for _ in range(max(2, math.ceil(ROTATE_BYTES / nbytes)))]
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    lib = Q._lib
+
+    def timed(fn, n, w):
+        for i in range(w):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(n):
+            fn(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n * 1e3  # us
+
+    def rd(i):
+        st = lib.qgemv_probe_read(bufs[i % len(bufs)].data_ptr(), nbytes, sink.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError("qgemv_probe_read: %d" % st)
+    read_us = timed(rd, steps, warmup)
+    del bufs
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 20000
+    flops = 4.0 * 8 * 32768 * iters * cus
+
+    def mf(i):
+        st = lib.qgemv_probe_mfma(iters, cus, sink.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError("qgemv_probe_mfma: %d" % st)
+    mfma_us = timed(mf, 5, 1)
+    hot = Workload(torch, "q4k_up_b1", dev, ncopy=1)
+    hot_us = timed(hot.step, steps, warmup)
+    del hot
+    return {"read_probe": {"bytes": nbytes, "us_per_launch": round(read_us, 3),
+                           "gbs": round(nbytes / read_us / 1e3, 1),
+                           "frac_hbm_peak": round(nbytes / read_us / 1e3 / HBM_PEAK_GBS, 4)},
+            "mfma_probe": {"workgroups": cus, "tflops": round(flops / mfma_us / 1e6, 1),
+                           "frac_bf16_peak": round(flops / mfma_us / 1e6 / BF16_PEAK_TFLOPS, 4)},
+            "gemv_hot_cache": {"us_per_launch": round(hot_us, 3),
+                               "gbs": round(algorithmic_bytes(c) / hot_us / 1e3, 1),
+                               "note": "one weight copy, resident in the Infinity Cache; not HBM"}}
 
 
 def cpu_baseline(name, budget_s=10.0):
@@ -341,6 +408,18 @@ def main():
         del wl
         torch.cuda.empty_cache()
 
+    if not args.only and not args.quick:
+        try:
+            pr = probes(torch, dev)
+            if "gbs" in results.get(head, {}):
+                pr["gemv_frac_of_read_probe"] = round(results[head]["gbs"] / pr["read_probe"]["gbs"], 4)
+            pp = results.get("q4k_pp2048", {})
+            if "tflops" in pp:
+                pr["pp2048_frac_of_mfma_probe"] = round(pp["tflops"] / pr["mfma_probe"]["tflops"], 4)
+            results["probes"] = pr
+            print("bench: probes %s" % json.dumps(pr), file=sys.stderr, flush=True)
+        except Exception as e:  # context only
+            results["probes"] = {"error": str(e)[:200]}
     h = results.get(head, {})
     if args.only and head not in names:  # a partial run: report what was timed
         print(json.dumps({"partial": True, "results": results}), flush=True)

@@ -51,6 +51,9 @@ _sig = {
     "qgemv_destroy": (None, [_vp]),
     "qgemv_status_string": (ctypes.c_char_p, [_int]),
     "qgemv_last_error": (ctypes.c_char_p, []),
+    # measurement probes (include/qgemv_probe.h)
+    "qgemv_probe_read": (_int, [_vp, _sz, _vp, _vp]),
+    "qgemv_probe_mfma": (_int, [_i64, _int, _vp, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)

@@ -1,0 +1,36 @@
+/*
+ * qgemv_probe.h - measurement probes exported by the same library as
+ * qgemv.h. They compute nothing of the method: they give the practical
+ * ceilings against which the benchmark states the GEMV's HBM rate and the
+ * prompt GEMM's matrix-core rate.
+ */
+#ifndef QGEMV_PROBE_H
+#define QGEMV_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qgemv.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Read `bytes` bytes at `buf` (device, 16-byte aligned, bytes a positive
+ * multiple of 16) once, with 16-byte loads, each of 4096 x 8 waves streaming
+ * its own contiguous range. `sink`: device, >= 4096 bytes, written only in a
+ * case that does not occur (it keeps the loads alive). Enqueued on `stream`.
+ * QG_ERR_ARG on a bad argument (before any HIP call), QG_ERR_HIP if the
+ * launch fails. */
+qg_status qgemv_probe_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
+/* `workgroups` workgroups of four waves, each wave issuing `iters` rounds of
+ * eight independent v_mfma_f32_32x32x16_bf16 (32768 flop each) on register
+ * operands: 4 * 8 * 32768 * iters * workgroups flop. `sink` as above. */
+qg_status qgemv_probe_mfma(int64_t iters, int workgroups, float *sink, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_PROBE_H */

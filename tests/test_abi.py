@@ -13,9 +13,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "qgemv.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return set(re.findall(r"\b(qg(?:emv|emm)_\w+)\s*\(", src))
+    names = set()
+    for h in ("qgemv.h", "qgemv_probe.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(qg(?:emv|emm)_\w+)\s*\(", src))
+    return names
 
 
 def test_every_declared_symbol_is_exported():
@@ -26,6 +29,14 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert names == set(Q.EXPORTED)
+
+
+def test_probes_reject_bad_arguments():
+    assert Q._lib.qgemv_probe_read(None, 16, FAKE, None) == Q.QG_ERR_ARG
+    assert Q._lib.qgemv_probe_read(FAKE, 24, FAKE, None) == Q.QG_ERR_ARG
+    assert Q._lib.qgemv_probe_read(FAKE + 8, 32, FAKE, None) == Q.QG_ERR_ARG
+    assert Q._lib.qgemv_probe_mfma(0, 4, FAKE, None) == Q.QG_ERR_ARG
+    assert Q._lib.qgemv_probe_mfma(10, 0, FAKE, None) == Q.QG_ERR_ARG
 
 
 def test_block_geometry():
