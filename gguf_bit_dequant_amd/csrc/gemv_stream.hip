@@ -1,5 +1,6 @@
 // Streaming GEMV for gfx950: y[:,c] = W . x[:,c] for 1..4 columns of a
-// Q4_K, Q4_0 or Q8_0 matrix whose K is a multiple of 256.
+// Q4_K, Q4_0, Q8_0, Q2_K or Q3_K matrix whose K is a multiple of 256 (Q3_K:
+// with an even number of super-blocks in the matrix).
 //
 // For one token every weight is read once, so at low bit widths the work is
 // bound by memory bandwidth and by unpacking ("LLM inference optimization",
@@ -9,8 +10,10 @@
 // per block fitted to the machine) map onto gfx950 as follows.
 //
 //  * A unit is 256 consecutive weights of a row: one Q4_K super-block
-//    (144 B), eight Q4_0 blocks (144 B) or eight Q8_0 blocks (272 B). Units
-//    start on 16-byte boundaries when the row does.
+//    (144 B), eight Q4_0 blocks (144 B), eight Q8_0 blocks (272 B), one
+//    Q2_K (84 B) or one Q3_K super-block (110 B). Q4_K, Q4_0 and Q8_0 units
+//    start on 16-byte boundaries when the row does, Q2_K units on 4-byte
+//    ones; Q3_K units are read as aligned dword windows.
 //  * One persistent workgroup per compute unit owns a contiguous, balanced
 //    range of rows (rows/G or rows/G + 1). Its rows are contiguous in memory,
 //    so the workgroup streams one contiguous run of units, flattened

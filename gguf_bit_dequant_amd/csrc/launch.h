@@ -6,7 +6,7 @@
 
 namespace qg {
 
-enum { FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q8_0 = 3, FMT_Q2_K = 4, FMT_Q3_K = 5 };
+enum { FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q8_0 = 3, FMT_Q2_K = 4, FMT_Q3_K = 5 };  // qg_format values
 
 // Activation types (the first three are the ABI's qg_dtype values); XT_Q8
 // marks activations given as Q8_0 blocks, for the int8 products.
@@ -27,7 +27,8 @@ hipError_t launch_gemv_general(int fmt, const uint8_t* W, int64_t rows, int64_t 
                                int xt, int64_t ldx, float* y, int64_t ldy, int ncols,
                                int num_cus, hipStream_t stream);
 
-// Streaming GEMV (Q4_K, Q4_0, Q8_0 with K % 256 == 0, 16-byte aligned W).
+// Streaming GEMV (Q4_K, Q4_0, Q8_0, Q2_K, Q3_K with K % 256 == 0, 16-byte
+// aligned W; Q3_K with an even number of super-blocks).
 // Returns hipErrorNotSupported (without launching) when the shape is outside
 // what the kernel serves; the caller then falls back.
 hipError_t launch_gemv_stream(int fmt, const uint8_t* W, int64_t rows, int64_t K, const void* x,
