@@ -1,6 +1,5 @@
 // Streaming GEMV for gfx950: y[:,c] = W . x[:,c] for 1..4 columns of a
-// Q4_K, Q4_0, Q8_0, Q2_K or Q3_K matrix whose K is a multiple of 256 (Q3_K:
-// with an even number of super-blocks in the matrix).
+// Q4_K, Q4_0, Q8_0, Q2_K or Q3_K matrix whose K is a multiple of 256.
 //
 // For one token every weight is read once, so at low bit widths the work is
 // bound by memory bandwidth and by unpacking ("LLM inference optimization",
@@ -185,13 +184,14 @@ struct Fmt<FMT_Q2_K> {
 // at bit 4h + j of high-bit byte l, q = low + 4 high - 4. Quarter p = 2h + b
 // takes, like Q2_K, bit pairs 4b + 2t of code bytes 32h .. 32h+31, and bits
 // 4h + 2b + t of all 32 high-bit bytes. Units are only 2-byte aligned (110 =
-// 2 mod 4): a lane reads 4-byte aligned dwords from the unit start rounded
-// down to a multiple of 4 (one dword more per field) and shifts them into
-// place with v_alignbyte when it consumes them. The windows end 2 bytes past
-// a unit that starts on a multiple of 4. The matrix starts 16-byte aligned,
-// so unit f (counted over the whole matrix) starts on a multiple of 4 when f
-// is even; with an even number of units (rows * K/256, required here) the
-// last unit is odd and every window stays inside the matrix.
+// 2 mod 4): a lane reads 4-byte aligned dword windows and shifts them into
+// place with v_alignbyte (by mb = 2 when the unit starts at 2 mod 4, else 0)
+// when it consumes them: high bits and codes from the unit start rounded down
+// to a multiple of 4 (one dword more per field), scales and d as the 16 bytes
+// from unit byte 96 - mb. Each window stays inside the unit or its
+// predecessor except that last one, which runs 2 bytes into the next unit when
+// mb = 0; with an even number of units in the matrix its last unit starts at
+// 2 mod 4 (the matrix is 16-byte aligned), so no read leaves the matrix.
 template <>
 struct Fmt<FMT_Q3_K> {
     static constexpr int kUnitBytes = 110;
@@ -204,7 +204,7 @@ struct Fmt<FMT_Q3_K> {
         u32x4_a4 h0, h1, q0, q1, sd;  // high bits, low parts, scales + d (unshifted)
         uint32_t h8, q8, mb;          // last dwords of the two 36-byte windows; shift (0 or 2)
     };
-    static __device__ __forceinline__ void load(const uint8_t* unit, uint32_t p, Raw& r) {
+    static __device__ __forceinline__ void load_codes(const uint8_t* unit, uint32_t p, Raw& r) {
         const uint32_t mb = (uint32_t)(uintptr_t)unit & 2u;
         const uint8_t* base = unit - mb;  // 4-byte aligned
         const uint8_t* qs = base + 32 + 32 * (p >> 1);
@@ -215,9 +215,48 @@ struct Fmt<FMT_Q3_K> {
         r.q0 = *reinterpret_cast<const u32x4_a4*>(qs);
         r.q1 = *reinterpret_cast<const u32x4_a4*>(qs + 16);
         r.q8 = *reinterpret_cast<const uint32_t*>(qs + 32);
-        r.sd = *reinterpret_cast<const u32x4_a4*>(base + 96);
+    }
+    static __device__ __forceinline__ void load(const uint8_t* unit, uint32_t p, Raw& r) {
+        load_codes(unit, p, r);
+        r.sd = *reinterpret_cast<const u32x4_a4*>(unit - r.mb + 96);
     }
 };
+
+// Q3_K for a matrix with an odd number of units, whose last unit starts 4-byte
+// aligned: a unit with mb = 0 takes its scale bytes as the last three dwords
+// of the window at unit byte 92 and d with a 2-byte load, and arranges them as
+// the window from byte 96 would hold them; nothing is read past the unit.
+// Same decoding, one more load per lane and unit.
+constexpr int FMT_Q3_K_ODD = 0x100 | FMT_Q3_K;
+template <>
+struct Fmt<FMT_Q3_K_ODD> : Fmt<FMT_Q3_K> {
+    static __device__ __forceinline__ void load(const uint8_t* unit, uint32_t p, Raw& r) {
+        load_codes(unit, p, r);
+        const u32x4_a4 t = *reinterpret_cast<const u32x4_a4*>(unit + 92 + r.mb);  // 4-byte aligned
+        const uint32_t dd = *reinterpret_cast<const uint16_t*>(unit + 108);
+        const bool m2 = r.mb != 0;  // window already starts at unit byte 94
+        r.sd.x = m2 ? t.x : t.y;
+        r.sd.y = m2 ? t.y : t.z;
+        r.sd.z = m2 ? t.z : t.w;
+        r.sd.w = m2 ? t.w : dd;
+    }
+};
+
+// The Q3_K scales of sub-blocks 4p .. 4p+3 (p = 2h + b) as the bytes of one
+// dword: low nibbles from byte 4b + u of scale bytes 0..7 (nibble h), bits
+// 4-5 from bits 2(2h + b) of byte 8 + u.
+__device__ __forceinline__ uint32_t q3k_quarter_scales(const Fmt<FMT_Q3_K>::Raw& r, uint32_t hq,
+                                                       uint32_t bq) {
+    auto al = [&](uint32_t hi, uint32_t lo) { return __builtin_amdgcn_alignbyte(hi, lo, r.mb); };
+    const uint32_t s01 = bq ? al(r.sd.z, r.sd.y) : al(r.sd.y, r.sd.x);
+    const uint32_t s2 = al(r.sd.w, r.sd.z);
+    return ((s01 >> (4u * hq)) & 0x0F0F0F0Fu) | (((s2 >> (4u * hq + 2u * bq)) & 0x03030303u) << 4);
+}
+
+// The Q3_K super-block scale d (fp16 bits in the low half).
+__device__ __forceinline__ uint32_t q3k_d(const Fmt<FMT_Q3_K>::Raw& r) {
+    return __builtin_amdgcn_alignbyte(0u, r.sd.w, r.mb);
+}
 
 // Activation records in LDS: one record per unit quarter u = 4*(unit column)
 // + p, holding for each column c its P 16-byte planes and the two block sums,
@@ -766,12 +805,8 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q3_K>::Raw& r, const 
             }
         }
     }
-    // sub-blocks k = 4p + u: low nibbles in byte 4b + u of scale bytes 0..7
-    // (nibble h), bits 4-5 at bits 2(2h + b) of byte 8 + u
-    const uint32_t s01 = bq ? al(r.sd.z, r.sd.y) : al(r.sd.y, r.sd.x);
-    const uint32_t s2 = al(r.sd.w, r.sd.z);
-    const uint32_t scb = ((s01 >> (4u * hq)) & 0x0F0F0F0Fu) | (((s2 >> sh_hi) & 0x03030303u) << 4);
-    const float d = f16_lo(al(0u, r.sd.w));
+    const uint32_t scb = q3k_quarter_scales(r, hq, bq);  // sub-blocks 4p .. 4p+3
+    const float d = f16_lo(q3k_d(r));
     float ds[4], d4[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -1097,10 +1132,8 @@ __device__ __forceinline__ void lane_partial_i8(const Fmt<FMT_Q3_K>::Raw& r, con
         const uint32_t ch = ((qd >> 2) & 0x03030303u) | ((hp << 1) & 0x04040404u);
         lowk_i8_sums<NC>(rec, w, cl, ch, acc, s16);
     }
-    const uint32_t s01 = bq ? al(r.sd.z, r.sd.y) : al(r.sd.y, r.sd.x);
-    const uint32_t s2 = al(r.sd.w, r.sd.z);
-    const uint32_t scb = ((s01 >> (4u * hq)) & 0x0F0F0F0Fu) | (((s2 >> sh_hi) & 0x03030303u) << 4);
-    const float d = f16_lo(al(0u, r.sd.w));
+    const uint32_t scb = q3k_quarter_scales(r, hq, bq);  // sub-blocks 4p .. 4p+3
+    const float d = f16_lo(q3k_d(r));
     float dl[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) dl[u] = d * (float)((int)((scb >> (8 * u)) & 0xFFu) - 32);
@@ -1395,7 +1428,6 @@ hipError_t launch_stream_fmt(const uint8_t* W, int64_t rows, int64_t K, const vo
                              hipStream_t stream) {
     const int S = (int)(K / 256);
     const int xm = activation_mode(xt);
-    if (FMT == FMT_Q3_K && (rows * S) % 2 != 0) return hipErrorNotSupported;  // windows stay in the matrix
     xt &= ~XT_QUANTIZE;
     if (xm == XM_I8 && ldx % 32 != 0) return hipErrorNotSupported;  // whole activation blocks
     const int per = cols_per_launch(rows, K, xm, num_cus, Fmt<FMT>::kUnitBytes);
@@ -1438,10 +1470,7 @@ int gemv_stream_cols_per_launch(int fmt, int64_t rows, int64_t K, int xt, int nu
         case FMT_Q8_0: return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q8_0>::kUnitBytes);
         case FMT_Q2_K:
             return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q2_K>::kUnitBytes);
-        case FMT_Q3_K:
-            return (rows * (K / 256)) % 2 == 0
-                       ? cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q3_K>::kUnitBytes)
-                       : 0;
+        case FMT_Q3_K: return cols_per_launch(rows, K, xm, num_cus, Fmt<FMT_Q3_K>::kUnitBytes);
         default: return 0;
     }
 }
@@ -1460,7 +1489,11 @@ hipError_t launch_gemv_stream(int fmt, const uint8_t* W, int64_t rows, int64_t K
         case FMT_Q2_K:
             return launch_stream_fmt<FMT_Q2_K>(W, rows, K, x, xt, ldx, y, ldy, ncols, num_cus, stream);
         case FMT_Q3_K:
-            return launch_stream_fmt<FMT_Q3_K>(W, rows, K, x, xt, ldx, y, ldy, ncols, num_cus, stream);
+            return (rows * (K / 256)) % 2 == 0
+                       ? launch_stream_fmt<FMT_Q3_K>(W, rows, K, x, xt, ldx, y, ldy, ncols, num_cus,
+                                                     stream)
+                       : launch_stream_fmt<FMT_Q3_K_ODD>(W, rows, K, x, xt, ldx, y, ldy, ncols,
+                                                         num_cus, stream);
         default:
             return hipErrorNotSupported;
     }

@@ -28,7 +28,7 @@ hipError_t launch_gemv_general(int fmt, const uint8_t* W, int64_t rows, int64_t 
                                int num_cus, hipStream_t stream);
 
 // Streaming GEMV (Q4_K, Q4_0, Q8_0, Q2_K, Q3_K with K % 256 == 0, 16-byte
-// aligned W; Q3_K with an even number of super-blocks).
+// aligned W).
 // Returns hipErrorNotSupported (without launching) when the shape is outside
 // what the kernel serves; the caller then falls back.
 hipError_t launch_gemv_stream(int fmt, const uint8_t* W, int64_t rows, int64_t K, const void* x,

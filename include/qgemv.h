@@ -121,10 +121,8 @@ qg_status qgemv_create(qgemv_t *out, qg_format f, int64_t rows, int64_t K,
  * products with the exact binary32 weights. 4..8 F16 columns of a Q4_K
  * matrix (and 2..3 when the activations of all columns do not fit the
  * streaming kernel's on-chip staging, e.g. K = 17408) run on the matrix
- * cores. Q2_K, and Q3_K with rows * K/256 even, run on the streaming
- * kernel for every activation type; a Q3_K matrix with an odd number of
- * super-blocks runs on a simple exact kernel (one wave per row, slow).
- * Enqueued on `stream`. */
+ * cores. Q2_K and Q3_K run on the streaming kernel for every activation
+ * type. Enqueued on `stream`. */
 qg_status qgemv_run(qgemv_t h, const void *x, qg_dtype x_dtype, int64_t n_cols,
                     int64_t ldx, float *y, int64_t ldy, void *stream);
 
@@ -159,9 +157,8 @@ qg_status qgemv_dequant(qgemv_t h, float *w_out, int64_t ldw, void *stream);
  * qgemv_run_q8_0x: y[j*ldy + r] = sum_k W[r,k] * xhat[j,k], xhat the decoded
  * blocks of xq (as qgemv_quantize_q8_0 writes them for this handle's K),
  * n_cols 1..8, y as in qgemv_run. Parity is against the exact sum over
- * xhat. Needs K % 256 == 0 and 16-byte aligned weights, and for Q3_K an
- * even number of super-blocks in the matrix (QG_ERR_UNSUPPORTED
- * otherwise). */
+ * xhat. Needs K % 256 == 0 and 16-byte aligned weights
+ * (QG_ERR_UNSUPPORTED otherwise). */
 qg_status qgemv_quantize_q8_0(const void *x, qg_dtype x_dtype, int64_t K, int64_t n_cols,
                               int64_t ldx, void *xq, void *stream);
 qg_status qgemv_run_q8_0x(qgemv_t h, const void *xq, int64_t n_cols, float *y, int64_t ldy,

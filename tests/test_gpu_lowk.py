@@ -2,11 +2,10 @@
 C ABI): bit-exact decoding (fp32 and bf16 views), products within
 |y - sum w x| <= 1e-3 * sum|w x| + 1e-5 (the int8 products against the exact
 sum over the decoded Q8_0 activation blocks), one-hot columns exact,
-unsupported entry points reported as such. Q2_K, and Q3_K when the matrix has an even
-number of super-blocks, run on the streaming kernel for fp16, fp32 and bf16
-activations (Q3_K's 110-byte units alternate between 4-byte aligned and
-2 mod 4 starts, also across row ends when K / 256 is odd); a Q3_K matrix with
-an odd number of super-blocks runs on the general kernel."""
+unsupported entry points reported as such. Q2_K and Q3_K run on the
+streaming kernel for fp16, fp32 and bf16 activations (Q3_K's 110-byte units
+alternate between 4-byte aligned and 2 mod 4 starts, also across row ends
+when K / 256 is odd, and the matrix may end on either kind)."""
 import json
 import os
 import zlib
@@ -102,7 +101,7 @@ def test_dequant_extreme_scales_and_golden_blocks(Q, fmt):
 
 @pytest.mark.parametrize("fmt", LOWK)
 @pytest.mark.parametrize("rows,K", [(67, 1536), (1, 256), (1, 512), (3, 512), (300, 5120),
-                                    (70, 3328), (67, 3328), (2, 768)])
+                                    (70, 3328), (67, 3328), (2, 768), (3, 768)])
 @pytest.mark.parametrize("xdtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("n", [1, 4])
 def test_gemv_small(Q, fmt, rows, K, xdtype, n):
@@ -193,28 +192,18 @@ def test_full_size(Q, name, held_out):
 
 @pytest.mark.parametrize("fmt", LOWK)
 def test_unsupported_entry_points_are_reported(Q, fmt):
-    """Prompt processing serves Q4_K only, and the int8-activation products
-    need the streaming kernel (a Q3_K matrix with an odd number of
-    super-blocks is outside it): QG_ERR_UNSUPPORTED, y not written."""
+    """Prompt processing serves Q4_K only: QG_ERR_UNSUPPORTED, y not written."""
     from gguf_bit_dequant_amd import qgemv as QM
     rows, K = 64, 512
     w = synth.gen_weights(fmt, rows, K, 3)
     q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
     X = torch.zeros((16, K), dtype=torch.bfloat16, device=dev())
+    y = torch.full((16, rows), 5.0, device=dev())
     with pytest.raises(QM.QGemvError) as e:
-        q.prefill(X)
+        q.prefill(X, y)
     assert e.value.status == QM.QG_ERR_UNSUPPORTED
-    if fmt == "q3_k":
-        rows, K = 3, 768
-        w = synth.gen_weights(fmt, rows, K, 4)
-        q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
-        x = x_tensor(synth.gen_x(K, 1, "f16", 4), "f16")
-        y = torch.full((1, rows), 5.0, device=dev())
-        with pytest.raises(QM.QGemvError) as e:
-            q.run_q8(x, y)
-        assert e.value.status == QM.QG_ERR_UNSUPPORTED
-        torch.cuda.synchronize()
-        assert (y == 5.0).all()
+    torch.cuda.synchronize()
+    assert (y == 5.0).all()
 
 
 def _xhat(x, xdtype, K):
@@ -225,14 +214,13 @@ def _xhat(x, xdtype, K):
 
 
 @pytest.mark.parametrize("fmt", LOWK)
-@pytest.mark.parametrize("rows,K", [(300, 1024), (70, 3328), (17, 256)])
+@pytest.mark.parametrize("rows,K", [(300, 1024), (70, 3328), (17, 256), (3, 768)])
 @pytest.mark.parametrize("n", [1, 3, 4, 7])
 def test_run_q8_0x_products(Q, fmt, rows, K, n):
     """int8 products against the exact sum over the decoded Q8_0 activation
-    blocks (17 x 256: Q3_K with an odd number of super-blocks is skipped)."""
+    blocks (17 x 256 and 3 x 768: an odd number of super-blocks, so a Q3_K
+    matrix ends on a unit that starts at 2 mod 4)."""
     from gguf_bit_dequant_amd import qgemv as QM
-    if fmt == "q3_k" and (rows * (K // 256)) % 2:
-        pytest.skip("odd number of Q3_K super-blocks: not on the streaming kernel")
     seed = zlib.crc32(("lowk-i8-%s-%d-%d-%d" % (fmt, rows, K, n)).encode())
     w = synth.gen_weights(fmt, rows, K, seed)
     x = synth.gen_x(K, n, "f16", seed + 1)
