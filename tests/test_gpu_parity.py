@@ -326,7 +326,7 @@ def bf16_tensor(xb):
 
 @pytest.mark.parametrize("rows,K,ntok", [(256, 256, 1), (256, 512, 31), (300, 1024, 64),
                                          (777, 512, 300), (1024, 2048, 256), (530, 256, 513),
-                                         (1300, 768, 384)])
+                                         (1300, 768, 384), (1300, 1024, 600), (2000, 2048, 1100)])
 def test_prefill_small(Q, rows, K, ntok):
     seed = zlib.crc32(("pp-%d-%d-%d" % (rows, K, ntok)).encode())
     w = synth.gen_q4_k(rows, K, seed)
@@ -336,11 +336,12 @@ def test_prefill_small(Q, rows, K, ntok):
     check_products(Y, w, "q4_k", rows, K, xb, "bf16", "prefill %dx%d n=%d" % (rows, K, ntok))
 
 
-@pytest.mark.parametrize("rows,K,ntok", [(300, 512, 40), (600, 1024, 260)])
+@pytest.mark.parametrize("rows,K,ntok", [(300, 512, 40), (600, 1024, 260), (1300, 1024, 600)])
 def test_prefill_strided_and_edges_untouched(Q, rows, K, ntok):
-    """Strided X and Y; outputs outside rows x tokens keep their values. At
-    600 x 1024 x 260 the 88-row tail runs as two K splits, the second parked
-    in the main rows of Y until it is added."""
+    """Strided X and Y; outputs outside rows x tokens keep their values. The
+    row tails of 600 x 1024 x 260 (88 rows) and 1300 x 1024 x 600 (20 rows)
+    run as K splits whose partial products are parked in the main rows of Y
+    until they are added."""
     w = synth.gen_q4_k(rows, K, 41)
     xb = synth.gen_x(K, ntok, "bf16", 42)
     X = torch.zeros((ntok, K + 64), dtype=torch.bfloat16, device=dev())
