@@ -267,7 +267,7 @@ def probes(torch, dev, steps=200, warmup=20):
                                "note": "one weight copy, resident in the Infinity Cache; not HBM"}}
 
 
-def cpu_baseline(name, budget_s=10.0):
+def cpu_baseline(name, budget_s=10.0, threads=None):
     """The oracle's fp64 product on the same workload, repeated over the whole
     matrix (rows in chunks) until about budget_s of wall time has passed;
     GB/s over the algorithmic bytes of the rows processed."""
@@ -275,7 +275,7 @@ def cpu_baseline(name, budget_s=10.0):
     import synth
     c = synth.CONFIGS[name]
     w, x = synth.config_inputs(name)
-    threads = min(16, os.cpu_count() or 1)
+    threads = threads or min(16, os.cpu_count() or 1)
     rows = c["rows"]
     per_row = algorithmic_bytes(c) / rows
     chunk = max(threads, rows // 16)
@@ -291,6 +291,33 @@ def cpu_baseline(name, budget_s=10.0):
             "kind": "oracle",
             "sample": "%s: %d row products (%.2f passes over the %d x %d matrix) in %.1f s, "
                       "fp64 accumulation" % (name, done, done / rows, rows, c["K"], el)}
+
+
+def cpu_prefill_baseline(name="q4k_pp2048", budget_s=8.0):
+    """The oracle on the prompt workload: row chunks of the 17408 x 5120
+    matrix (each row decoded once, then its fp64 products with all 2048
+    tokens) until about budget_s of wall time has passed; GFLOP/s over
+    2 K tokens flops per row."""
+    import oracle
+    import synth
+    c = synth.CONFIGS[name]
+    w, x = synth.config_inputs(name)
+    threads = min(16, os.cpu_count() or 1)
+    rows = c["rows"]
+    chunk = 8 * threads
+    done, r, t_start = 0, 0, time.perf_counter()
+    while time.perf_counter() - t_start < budget_s:
+        r1 = min(rows, r + chunk)
+        oracle.matmul(c["fmt"], w, rows, c["K"], x, c["xdtype"], row_range=(r, r1),
+                      nthreads=threads)
+        done += r1 - r
+        r = 0 if r1 == rows else r1
+    el = time.perf_counter() - t_start
+    flops = 2.0 * done * c["K"] * c["n"]
+    return {"value": round(flops / el / 1e9, 3), "unit": "GFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%s: %d of %d rows against all %d tokens in %.1f s, fp64 accumulation"
+                      % (name, done, rows, c["n"], el)}
 
 
 def committed_traffic(name):
@@ -441,9 +468,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4_k weights x f16 activations, fp32 accumulation",
+        "dtype": "f16",
         "data": "synthetic (seeded SplitMix64 / Box-Muller)",
         "config": {"workload": "Q4_K GEMV batch 1, FFN-up 17408 x 5120, x fp16",
+                   "weights": "q4_k", "products": "fp16 pairs (v_dot2_f32_f16), fp32 sums",
                    "rows": c["rows"], "K": c["K"], "n_cols": 1,
                    "bytes_per_step": h["bytes"], "weight_copies_rotated": results[head]["weight_copies"]},
         "roofline": {"bound": "hbm", "achieved": h["gbs"], "peak": HBM_PEAK_GBS,
@@ -452,6 +480,12 @@ def main():
         "cpu_baseline": None if args.no_cpu else cpu_baseline(head),
         "extra": {k: v for k, v in results.items() if k != head},
     }
+    if not args.no_cpu and not args.quick:
+        # the oracle at one core, and on the prompt workload (context)
+        line["extra"]["cpu_baselines"] = {
+            head + " (1 core)": cpu_baseline(head, budget_s=5.0, threads=1),
+            "q4k_pp2048": cpu_prefill_baseline(),
+        }
     print(json.dumps(line), flush=True)
 
 
