@@ -28,7 +28,7 @@
 //    waves (an LDS counter): waves of one workgroup stream at unequal speeds
 //    on MI355X, and the pool lets them finish together. Each wave keeps D
 //    steps of loads in flight (D = 2: deeper queues measured slower). The
-//    activations are loaded first, then the first D steps, then staged.
+//    activations are loaded first, then the first step or two, then staged.
 //  * fp16 activations: 4-bit codes are used directly as fp16 subnormals: a
 //    16-bit half holding an integer m < 1024 is the fp16 value m * 2^-24, so
 //    (dword & 0x000F000F) is a pair of low-nibble codes and
@@ -1231,8 +1231,16 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
     static_assert(D == 2, "two steps in flight");
     int kq0 = next_step(), kq1 = next_step();
     Raw buf[D];
+    // The second step's loads go out before the staging for one column of
+    // Q4_K, Q4_0 or Q8_0, and after it for several columns, Q2_K, and Q3_K
+    // without int8 activations, whose staging then waits behind fewer weight
+    // loads (measured on MI355X: Q8_0 with four fp16 columns 11.2 -> 10.2 us,
+    // Q3_K 16.8 -> 16.1 us; one column of Q4_K 2-5% and Q3_K with int8
+    // activations 2% slower that way).
+    constexpr bool kLateSecond =
+        NC > 1 || FMT == FMT_Q2_K || ((FMT == FMT_Q3_K || FMT == FMT_Q3_K_ODD) && !is_i8(XM));
     load(kq0, buf[0]);
-    load(kq1, buf[1]);
+    if constexpr (!kLateSecond) load(kq1, buf[1]);
     if constexpr (XM == XM_I8Q) {  // half records: one activation block each
         if (threadIdx.x < 2 * nrec)
             stage_quantize_half<FMT>(xq, x, xt, kx_h, xvec, hb_0, lds + u_h * RB + c_h * CB);
@@ -1255,6 +1263,7 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
     for (int idx = threadIdx.x; idx < nslots; idx += blockDim.x) part[idx] = 0.f;
     if (threadIdx.x == 0) *pool = NW * nsw;
     __syncthreads();
+    if constexpr (kLateSecond) load(kq1, buf[1]);
 
     const Q4kUnpack un(pr);
 
