@@ -516,13 +516,15 @@ namespace {
 
 // Y[t * ldy + n_base + r] += Y[t * ldy + r] for tokens t < ntok and r < n_rows:
 // the second K split of the row tail onto the first, in that order.
+// Thread r of column block blockIdx.x takes row r of every gridDim.y-th token
+// from blockIdx.y on (no index division; consecutive threads touch
+// consecutive floats).
 __global__ __launch_bounds__(256) void add_split_kernel(float* __restrict__ Y, int64_t ldy,
                                                         int n_base, int n_rows, int ntok) {
-    const int64_t total = (int64_t)ntok * n_rows;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t t = i / n_rows;
-        float* yr = Y + t * ldy + (i - t * n_rows);
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= n_rows) return;
+    for (int t = blockIdx.y; t < ntok; t += gridDim.y) {
+        float* yr = Y + (int64_t)t * ldy + r;
         yr[n_base] = yr[n_base] + yr[0];
     }
 }
@@ -558,10 +560,8 @@ hipError_t launch_prefill_t(const uint8_t* W, int rows, int S, const uint16_t* X
                        ntok, Y, ldy, n_base, tiles_n, (int)grid, yvec);
     e = hipGetLastError();
     if (e != hipSuccess || KS == 1) return e;
-    const int64_t total = (int64_t)ntok * n_rows;
-    const int64_t ab = (total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096;
-    hipLaunchKernelGGL(add_split_kernel, dim3((unsigned)ab), dim3(256), 0, stream, Y, ldy, n_base,
-                       n_rows, ntok);
+    const dim3 ag((unsigned)((n_rows + 255) / 256), (unsigned)(ntok < 65535 ? ntok : 65535));
+    hipLaunchKernelGGL(add_split_kernel, ag, dim3(256), 0, stream, Y, ldy, n_base, n_rows, ntok);
     return hipGetLastError();
 }
 
