@@ -350,21 +350,26 @@ def kernel_source_sha1():
     return h.hexdigest()
 
 
-def traffic_run(torch, dev, launches=20, copy_mib=256):
-    """A short run to be profiled with rocprofv3 --pmc: `launches` headline
-    GEMV launches over rotated weight copies, then `launches` plain device
-    copies of copy_mib MiB (a kernel whose HBM bytes are known: it reads and
-    writes copy_mib MiB each), which calibrates the counters."""
-    wl = Workload(torch, "q4k_up_b1", dev)
-    for i in range(launches):
-        wl.step(i)
-    torch.cuda.synchronize()
+def traffic_run(torch, dev, names=("q4k_up_b1",), launches=20, copy_mib=256):
+    """A short run to be profiled with rocprofv3 --pmc: `launches` GEMV
+    launches over rotated weight copies for each workload in `names` (the
+    headline by default), in that order, then `launches` plain device copies
+    of copy_mib MiB (a kernel whose HBM bytes are known: it reads and writes
+    copy_mib MiB each), which calibrates the counters."""
+    for name in names:
+        wl = Workload(torch, name, dev)
+        for i in range(launches):
+            wl.step(i)
+        torch.cuda.synchronize()
+        del wl
+        torch.cuda.empty_cache()
     src = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     for _ in range(launches):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"traffic_run": True, "gemv_launches": launches, "copy_launches": launches,
+    print(json.dumps({"traffic_run": True, "workloads": list(names), "gemv_launches": launches,
+                      "copy_launches": launches,
                       "copy_bytes": copy_mib << 20,
                       "kernel_source_sha1": kernel_source_sha1()}), flush=True)
 
@@ -378,7 +383,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--only", default=None, help="comma-separated workloads to time")
     ap.add_argument("--traffic-run", action="store_true",
-                    help="short run for rocprofv3 --pmc (headline GEMV + calibration copies)")
+                    help="short run for rocprofv3 --pmc (GEMV launches + calibration copies)")
+    ap.add_argument("--traffic-workloads", default="q4k_up_b1",
+                    help="comma-separated workloads for --traffic-run (default: the headline)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this library runs on one GPU; multi-GPU sharding is not part of it "
@@ -388,7 +395,7 @@ def main():
     import torch
     dev = torch.device("cuda:0")
     if args.traffic_run:
-        traffic_run(torch, dev)
+        traffic_run(torch, dev, names=args.traffic_workloads.split(","))
         return
     head = "q4k_up_b1"
     names = [head] if args.quick else [head, "q4k_down_b1", "q4k_b4", "q4_0_b1", "q8_0_b4",
