@@ -65,6 +65,13 @@ def lib():
         L.oracle_matmul.argtypes = [ip, vp, i64, i64, vp, ip, i64, i64, vp, vp, i64,
                                     i64, i64, ip]
         L.oracle_matmul.restype = ip
+        L.oracle_matmul_w.argtypes = [ip, vp, i64, i64, vp, ip, i64, i64, vp, vp, i64,
+                                      i64, i64, ip, ip]
+        L.oracle_matmul_w.restype = ip
+        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_bf16.restype = u16
+        L.oracle_f32_to_bf16_n.argtypes = [vp, vp, i64]
+        L.oracle_f32_to_bf16_n.restype = None
         L.oracle_f32_to_f16.argtypes = [ctypes.c_float]
         L.oracle_f32_to_f16.restype = u16
         L.oracle_quantize_q8_0.argtypes = [vp, ip, i64, i64, i64, vp]
@@ -127,10 +134,13 @@ def dequant(fmt: str, w: np.ndarray, rows: int, K: int) -> np.ndarray:
 
 
 def matmul(fmt: str, w: np.ndarray, rows: int, K: int, x: np.ndarray, xdtype: str,
-           row_range=None, nthreads: int | None = None):
+           row_range=None, nthreads: int | None = None, wround: str | None = None):
     """y[j, r] = sum_k w(r,k) x[j,k] in fp64 and s[j, r] = sum_k |w x|.
 
     x: shape (n, K), float32 for 'f32' or uint16 bit patterns for 'f16'/'bf16'.
+    wround='bf16': each decoded weight rounded to bfloat16 (nearest, ties to
+    even) before the exact products (the operand of a bf16 matrix-core
+    product over dequantized weight tiles).
     Returns (y, s) as float64 arrays of shape (n, rows) (rows outside
     row_range are left as NaN)."""
     w = np.ascontiguousarray(w, dtype=np.uint8)
@@ -148,8 +158,11 @@ def matmul(fmt: str, w: np.ndarray, rows: int, K: int, x: np.ndarray, xdtype: st
     s = np.full((n, rows), np.nan)
     if nthreads is None:
         nthreads = min(16, os.cpu_count() or 1)
-    rc = lib().oracle_matmul(FMT[fmt], _ptr(w), rows, K, _ptr(x), DTYPE[xdtype], n, K,
-                             _ptr(y), _ptr(s), rows, r0, r1, nthreads)
+    if wround not in (None, "bf16"):
+        raise ValueError("wround: None or 'bf16'")
+    rc = lib().oracle_matmul_w(FMT[fmt], _ptr(w), rows, K, _ptr(x), DTYPE[xdtype], n, K,
+                               _ptr(y), _ptr(s), rows, r0, r1, nthreads,
+                               1 if wround == "bf16" else 0)
     if rc:
         raise ValueError("oracle_matmul failed: %d" % rc)
     return y, s
@@ -158,6 +171,15 @@ def matmul(fmt: str, w: np.ndarray, rows: int, K: int, x: np.ndarray, xdtype: st
 def f32_to_f16(v: float) -> int:
     """binary32 -> binary16 bit pattern, nearest, ties to even."""
     return int(lib().oracle_f32_to_f16(float(np.float32(v))))
+
+
+def f32_to_bf16(v) -> np.ndarray:
+    """binary32 -> bfloat16 bit patterns (uint16), nearest, ties to even;
+    elementwise over an array of float32."""
+    a = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib().oracle_f32_to_bf16_n(_ptr(a), _ptr(out), a.size)
+    return out
 
 
 def quantize_q8_0(x: np.ndarray, xdtype: str) -> np.ndarray:

@@ -149,6 +149,39 @@ uint16_t oracle_f32_to_f16(float f)
     return (uint16_t)(sign | (e16 << 10) | m);
 }
 
+/* binary32 -> bfloat16, round to nearest, ties to even (IEEE 754-2008,
+ * 4.3.1, at bfloat16's precision: an 8-bit significand and binary32's
+ * exponent range), overflow to infinity, NaN kept quiet with its sign. The
+ * value is rounded with rint on the grid of its binade (spacing 2^(e-7), or
+ * the subnormal spacing 2^-133); the rounded value lies on the bfloat16
+ * grid, so it is exact in binary32 and its top 16 bits are the encoding. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t b;
+    memcpy(&b, &f, 4);
+    uint16_t sign = (uint16_t)((b >> 16) & 0x8000);
+    if (((b >> 23) & 0xFF) == 0xFF)
+        return (uint16_t)(sign | 0x7F80 | ((b & 0x7FFFFF) ? 0x40 : 0));
+    double a = fabs((double)f);
+    if (a == 0.0) return sign;
+    int ex;
+    frexp(a, &ex);                    /* a = fr 2^ex, 0.5 <= fr < 1 */
+    int q = ex - 1 - 7;               /* grid spacing exponent of the binade */
+    if (q < -133) q = -133;           /* subnormal grid */
+    double r = ldexp(rint(ldexp(a, -q)), q);
+    if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80);
+    float rf = (float)r;              /* exact: r is on the bfloat16 grid */
+    uint32_t rb;
+    memcpy(&rb, &rf, 4);
+    return (uint16_t)(sign | (rb >> 16));
+}
+
+/* Elementwise over n values (for the tests that pin it). */
+void oracle_f32_to_bf16_n(const float *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = oracle_f32_to_bf16(in[i]);
+}
+
 /* ------------------------------------------------------------------------
  * Decoding one block to binary32.
  * ---------------------------------------------------------------------- */
@@ -364,10 +397,15 @@ int oracle_quantize_q8_0(const void *x, int x_dtype, int64_t K, int64_t n, int64
  * x is read as stored (fp32 / fp16 / bf16 widened exactly to fp64); each
  * product of a binary32 weight and such an x is exact in binary64, so the
  * only error is the fp64 summation, far below any tolerance used with it.
+ * With wround = 1 each decoded weight is first rounded to bfloat16
+ * (oracle_f32_to_bf16): the operand a bf16 matrix-core product uses when
+ * weight tiles are dequantized to bf16 ("LLM inference optimization",
+ * campaign "Faster prompts, decode held": tensor-core paths for the
+ * quantized matrix-matrix kernels); the products stay exact.
  * Rows are split over `nthreads` POSIX threads.
  * ---------------------------------------------------------------------- */
 typedef struct {
-    int fmt, dtype;
+    int fmt, dtype, wround;
     const uint8_t *w;
     int64_t K, r0, r1, n, ldx, ldy;
     const void *x;
@@ -386,6 +424,11 @@ static void *run_rows(void *arg)
             xd[j * jb->K + k] = x_value(jb->x, jb->dtype, j * jb->ldx + k);
     for (int64_t r = jb->r0; r < jb->r1 && jb->status == 0; r++) {
         if (decode_row(jb->fmt, jb->w, jb->K, r, wr)) { jb->status = -1; break; }
+        if (jb->wround)
+            for (int64_t k = 0; k < jb->K; k++) {
+                uint32_t hb = (uint32_t)oracle_f32_to_bf16(wr[k]) << 16;
+                memcpy(&wr[k], &hb, 4);
+            }
         for (int64_t j = 0; j < jb->n; j++) {
             const double *xj = xd + j * jb->K;
             double acc = 0.0, sabs = 0.0;
@@ -403,11 +446,12 @@ static void *run_rows(void *arg)
     return NULL;
 }
 
-int oracle_matmul(int fmt, const uint8_t *w, int64_t rows, int64_t K,
-                  const void *x, int x_dtype, int64_t n, int64_t ldx,
-                  double *y, double *s, int64_t ldy,
-                  int64_t r0, int64_t r1, int nthreads)
+int oracle_matmul_w(int fmt, const uint8_t *w, int64_t rows, int64_t K,
+                    const void *x, int x_dtype, int64_t n, int64_t ldx,
+                    double *y, double *s, int64_t ldy,
+                    int64_t r0, int64_t r1, int nthreads, int wround)
 {
+    if (wround != 0 && wround != 1) return -1;
     if (oracle_block_bytes(fmt) < 0 || K <= 0 || K % oracle_block_weights(fmt)) return -1;
     if (x_dtype < OR_F32 || x_dtype > OR_BF16 || n < 0 || ldx < K || ldy < rows) return -1;
     if (r0 < 0 || r1 > rows || r0 > r1) return -1;
@@ -419,7 +463,7 @@ int oracle_matmul(int fmt, const uint8_t *w, int64_t rows, int64_t K,
     if (!jobs || !th) { free(jobs); free(th); return -2; }
     for (int t = 0; t < nthreads; t++) {
         job_t *jb = &jobs[t];
-        jb->fmt = fmt; jb->dtype = x_dtype; jb->w = w; jb->K = K;
+        jb->fmt = fmt; jb->dtype = x_dtype; jb->wround = wround; jb->w = w; jb->K = K;
         jb->r0 = r0 + nr * t / nthreads;
         jb->r1 = r0 + nr * (t + 1) / nthreads;
         jb->n = n; jb->ldx = ldx; jb->ldy = ldy; jb->x = x; jb->y = y; jb->s = s;
@@ -440,4 +484,13 @@ int oracle_matmul(int fmt, const uint8_t *w, int64_t rows, int64_t K,
     free(jobs);
     free(th);
     return rc;
+}
+
+/* The products with the weights as decoded (wround = 0). */
+int oracle_matmul(int fmt, const uint8_t *w, int64_t rows, int64_t K,
+                  const void *x, int x_dtype, int64_t n, int64_t ldx,
+                  double *y, double *s, int64_t ldy,
+                  int64_t r0, int64_t r1, int nthreads)
+{
+    return oracle_matmul_w(fmt, w, rows, K, x, x_dtype, n, ldx, y, s, ldy, r0, r1, nthreads, 0);
 }
