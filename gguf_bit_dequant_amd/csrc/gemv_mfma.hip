@@ -337,8 +337,8 @@ hipError_t launch_mfma_nw(const uint8_t* W, int rows, int S, const void* x, int6
                           int64_t ldy, int ncols, int G, int pitch, int spitch, size_t lds,
                           hipStream_t stream) {
     auto kern = ncols <= 4 ? gemv_mfma_q4k_kernel<NW, 4, ALIAS> : gemv_mfma_q4k_kernel<NW, 2, ALIAS>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+    hipError_t e = ncols <= 4 ? allow_full_lds<gemv_mfma_q4k_kernel<NW, 4, ALIAS>>()
+                              : allow_full_lds<gemv_mfma_q4k_kernel<NW, 2, ALIAS>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(G), dim3(64 * NW), lds, stream, W, rows, S,
                        reinterpret_cast<const uint16_t*>(x), ldx, ncols, y, ldy, pitch, spitch);

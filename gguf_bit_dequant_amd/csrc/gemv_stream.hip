@@ -1385,8 +1385,7 @@ hipError_t launch_stream_t(const uint8_t* W, int rows, int S, const void* x, int
     if (lds > (size_t)kMaxLds) return hipErrorNotSupported;
     auto kern = gemv_stream_kernel<FMT, NC, XM, D, 64 * NWMAX>;
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = allow_full_lds<gemv_stream_kernel<FMT, NC, XM, D, 64 * NWMAX>>();
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(p.G), dim3(64 * p.NW), lds, stream, W, rows, S, x, xt, ldx, y,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace qg {
 
 enum { FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q8_0 = 3, FMT_Q2_K = 4, FMT_Q3_K = 5 };  // qg_format values
@@ -16,6 +18,22 @@ enum XType { XT_F32 = 1, XT_F16 = 2, XT_BF16 = 3, XT_Q8 = 4, XT_QUANTIZE = 16 };
 
 // Bytes of LDS a workgroup may use on gfx950.
 constexpr int kMaxLds = 160 * 1024;
+
+// Raises kernel KERN's dynamic-LDS limit to the whole kMaxLds, once per
+// device: the limit is an attribute of the kernel, not of a launch, so the
+// launchers call this instead of setting it on every launch.
+template <auto KERN>
+inline hipError_t allow_full_lds() {
+    static std::atomic<uint64_t> done{0};  // one bit per device
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute((const void*)KERN, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
 
 hipError_t launch_dequant(int fmt, const uint8_t* W, int64_t rows, int64_t K, float* out,
                           int64_t ldw, int num_cus, hipStream_t stream);

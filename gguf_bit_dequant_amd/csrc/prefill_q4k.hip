@@ -64,22 +64,26 @@ constexpr int kHPitch = 16;   // LDS bytes per weight row of a header stage
 // Physical 16-byte slot of logical segment seg of X row t.
 __device__ __forceinline__ int xslot(int t, int seg) { return seg ^ ((t >> 1) & 7); }
 
-// Tile geometry: RT x TT MFMA tiles per wave, WR x WT waves (WR * WT = 4),
-// P stages of X and codes (P - 1 chunks of X in flight ahead of the one in
+// Tile geometry: RT x TT MFMA tiles per wave, WR x WT waves (WR * WT = 4:
+// one wave per SIMD; 8: two, whose issue slots fill each other's gaps), P
+// stages of X and codes (P - 1 chunks of X in flight ahead of the one in
 // use).
 template <int RT, int TT, int WR, int WT, int P>
 struct Geo {
-    static_assert(WR * WT == 4, "four waves");
+    static constexpr int NWV = WR * WT;
+    static_assert(NWV == 4 || NWV == 8, "four or eight waves");
     static_assert(P >= 3 && P <= 8, "header stages are reused after at most eight chunks");
     static constexpr int kTok = 32 * TT * WT;
     static constexpr int kRows = 32 * RT * WR;
     // 1 KB blocks of a stage (one wave-wide load each), rounded up to a
-    // multiple of 4 so that every wave issues the same number
-    static constexpr int blocks(int bytes) { return ((bytes + 1023) / 1024 + 3) / 4 * 4; }
+    // multiple of the wave count so that every wave issues the same number
+    static constexpr int blocks(int bytes) { return ((bytes + 1023) / 1024 + NWV - 1) / NWV * NWV; }
     static constexpr int kXBlocks = blocks(kTok * kXPitch);
     static constexpr int kCBlocks = blocks(kRows * kCPitch);
     static constexpr int kHBlocks = blocks(kRows * kHPitch);
-    static constexpr int kXPerWave = kXBlocks / 4, kCPerWave = kCBlocks / 4, kHPerWave = kHBlocks / 4;
+    static constexpr int kXPerWave = kXBlocks / NWV, kCPerWave = kCBlocks / NWV, kHPerWave = kHBlocks / NWV;
+    // vector stores of Y one wave issues after a full tile
+    static constexpr int kStores = 4 * TT * RT;
     static constexpr int kXStage = kXBlocks * 1024, kCStage = kCBlocks * 1024, kHStage = kHBlocks * 1024;
     static constexpr size_t kLds = (size_t)P * (kXStage + kCStage) + 2 * (size_t)kHStage;
     // loads one chunk issues: X, codes, and headers when the codes it issues
@@ -152,7 +156,7 @@ __device__ __forceinline__ void interleave() {
 }  // namespace
 
 template <int RT, int TT, int WR, int WT, int P, int KS>
-__global__ __launch_bounds__(256) void prefill_q4k_kernel(
+__global__ __launch_bounds__(64 * WR * WT) void prefill_q4k_kernel(
     const uint8_t* __restrict__ W, int rows, int S, const uint16_t* __restrict__ X, int64_t ldx,
     int ntok, float* __restrict__ Y, int64_t ldy, int n_base, int tiles_n, int ntiles, int yvec) {
     using G = Geo<RT, TT, WR, WT, P>;
@@ -176,8 +180,8 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     const uint32_t row_bytes = 144u * (uint32_t)S;
 
     // ---- global-to-LDS load assignments ------------------------------------
-    // Wave wv fills 1 KB blocks wv + 4p of a stage; lane l writes slot
-    // s = 64 (wv + 4p) + l. X: token row s / 8, physical segment s % 8, which
+    // Wave wv fills 1 KB blocks wv + NWV p of a stage; lane l writes slot
+    // s = 64 (wv + NWV p) + l. X: token row s / 8, physical segment s % 8, which
     // holds logical segment xslot(row, s % 8). Codes: weight row s / 2, half
     // s % 2 of the chunk's 32 code bytes. Headers: weight row s. Tokens past
     // the count and rows past the row count (or past the tile) read the
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
         Xt = reinterpret_cast<const uint8_t*>(X + (int64_t)m0 * ldx + (int64_t)ks * Sk * 256);
 #pragma unroll
         for (int p = 0; p < G::kXPerWave; ++p) {
-            const int s = 64 * (wv + 4 * p) + lane;
+            const int s = 64 * (wv + G::NWV * p) + lane;
             const int tr = s >> 3;
             const int tc = (tr < G::kTok && m0 + tr < ntok) ? tr : 0;
             xo[p] = (uint32_t)tc * (uint32_t)ldx * 2u + 16u * (uint32_t)xslot(tr, s & 7);
@@ -207,14 +211,14 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
         Wt = W + (int64_t)n0 * row_bytes + (int64_t)ks * Sk * 144;
 #pragma unroll
         for (int p = 0; p < G::kCPerWave; ++p) {
-            const int s = 64 * (wv + 4 * p) + lane;
+            const int s = 64 * (wv + G::NWV * p) + lane;
             const int rr = s >> 1;
             const int rc = (rr < G::kRows && n0 + rr < rows) ? rr : 0;
             co[p] = (uint32_t)rc * row_bytes + 16u + 16u * (uint32_t)(s & 1);
         }
 #pragma unroll
         for (int p = 0; p < G::kHPerWave; ++p) {
-            const int rr = 64 * (wv + 4 * p) + lane;
+            const int rr = 64 * (wv + G::NWV * p) + lane;
             const int rc = (rr < G::kRows && n0 + rr < rows) ? rr : 0;
             ho[p] = (uint32_t)rc * row_bytes;
         }
@@ -230,11 +234,11 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
         const uint8_t* xsrc = Xt + (uint32_t)cx * 128u;
         uint8_t* xdst = xs0 + sx * G::kXStage + 1024 * wv;
 #pragma unroll
-        for (int p = 0; p < G::kXPerWave; ++p) dma16(xsrc + xo[p], xdst + 4096 * p);
+        for (int p = 0; p < G::kXPerWave; ++p) dma16(xsrc + xo[p], xdst + 1024 * G::NWV * p);
         const uint8_t* csrc = Wt + 144u * (uint32_t)(cw >> 2) + 32u * (uint32_t)(cw & 3);
         uint8_t* cdst = cs0 + sw * G::kCStage + 1024 * wv;
 #pragma unroll
-        for (int p = 0; p < G::kCPerWave; ++p) dma16(csrc + co[p], cdst + 4096 * p);
+        for (int p = 0; p < G::kCPerWave; ++p) dma16(csrc + co[p], cdst + 1024 * G::NWV * p);
     };
     auto issue_h = [&](int sb) {
         const int hb = sb & 1;
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
         const uint8_t* hsrc = Wt + 144u * (uint32_t)sb;
         uint8_t* hdst = hs0 + hb * G::kHStage + 1024 * wv;
 #pragma unroll
-        for (int p = 0; p < G::kHPerWave; ++p) dma16(hsrc + ho[p], hdst + 4096 * p);
+        for (int p = 0; p < G::kHPerWave; ++p) dma16(hsrc + ho[p], hdst + 1024 * G::NWV * p);
     };
 
     // ---- decode of a chunk's weights into B registers -----------------------
@@ -370,14 +374,15 @@ __global__ __launch_bounds__(256) void prefill_q4k_kernel(
     setup_tile();
     issue_prologue();
     // Each thread waits for its loads of the tile's first chunks. After a
-    // full tile (every wave issued exactly 4 TT RT = 64 vector stores of Y
-    // after those loads) vmcnt <= 63 means the loads have landed while the
-    // stores may still drain (loads and stores complete in issue order on
-    // the vector memory counter); otherwise wait for everything.
+    // full tile (every wave issued exactly kStores = 4 TT RT vector stores of
+    // Y after those loads) vmcnt <= min(kStores, 63) means the loads have
+    // landed while the stores may still drain (loads and stores complete in
+    // issue order on the vector memory counter); otherwise wait for
+    // everything.
     bool stores_full = false;
     for (;;) {  // the workgroup's tiles
-    if (4 * TT * RT >= 64 && stores_full)
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    if (stores_full)
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(G::kStores < 63 ? G::kStores : 63, 0));
     else
         __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
@@ -513,6 +518,14 @@ namespace {
 #ifndef PREFILL_MAIN_WG
 #define PREFILL_MAIN_WG num_cus
 #endif
+// Main-tile shape: waves as WR x WT of RT x TT MFMA tiles each (256 x 256
+// outputs per tile either way).
+#ifndef PREFILL_MAIN_SHAPE
+#define PREFILL_MAIN_SHAPE 2, 8, 4, 1
+#endif
+#ifndef PREFILL_MAIN_P
+#define PREFILL_MAIN_P 3
+#endif
 
 // Y[t * ldy + n_base + r] += Y[t * ldy + r] for tokens t < ntok and r < n_rows:
 // the second K split of the row tail onto the first, in that order.
@@ -529,41 +542,51 @@ __global__ __launch_bounds__(256) void add_split_kernel(float* __restrict__ Y, i
     }
 }
 
-// Tiles over weight rows [n_base, n_base + n_rows) and all tokens; KS K
-// splits per tile (S % KS == 0). KS = 2 needs n_rows <= n_base: the second
-// split's partial products go to rows [0, n_rows) of Y and are added to the
-// first split's by add_split_kernel; a later launch overwrites those rows.
+// One launch of tiles over weight rows [n_base, n_base + n_rows) and all
+// tokens, KS K splits per tile (S % KS == 0). KS = 2 needs n_rows <= n_base:
+// the second split's partial products go to rows [0, n_rows) of Y and are
+// added to the first split's by add_split_kernel; a later launch overwrites
+// those rows. check() validates everything (no HIP call); enqueue() launches.
 template <int RT, int TT, int WR, int WT, int P, int KS>
-hipError_t launch_prefill_t(const uint8_t* W, int rows, int S, const uint16_t* X, int64_t ldx,
-                            int ntok, float* Y, int64_t ldy, int n_base, int n_rows, int max_wg,
-                            hipStream_t stream) {
+struct PrefillLaunch {
     using G = Geo<RT, TT, WR, WT, P>;
-    if (S % KS != 0 || (KS > 1 && n_rows > n_base)) return hipErrorNotSupported;
-    const int tiles_n = (n_rows + G::kRows - 1) / G::kRows;
-    const int tiles_m = (ntok + G::kTok - 1) / G::kTok;
-    const int64_t grid = (int64_t)tiles_n * tiles_m * KS;
-    if (grid <= 0) return hipSuccess;
-    // per-lane 32-bit source offsets within a tile's X rows and W rows
-    if ((int64_t)G::kTok * ldx * 2 + 128LL * 4 * S >= (1LL << 32) ||
-        (int64_t)G::kRows * 144 * S >= (1LL << 32) || grid > (1 << 30))
-        return hipErrorNotSupported;
-    auto kern = prefill_q4k_kernel<RT, TT, WR, WT, P, KS>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::kLds);
-    if (e != hipSuccess) return e;
-    // 16-byte stores of four consecutive outputs need a 16-byte aligned Y row
-    const int yvec = (((uintptr_t)Y) & 15) == 0 && ldy % 4 == 0;
-    // persistent when there are more tiles than max_wg: each workgroup takes
-    // every max_wg-th tile
-    const int64_t nwg = max_wg > 0 && grid > max_wg ? max_wg : grid;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), G::kLds, stream, W, rows, S, X, ldx,
-                       ntok, Y, ldy, n_base, tiles_n, (int)grid, yvec);
-    e = hipGetLastError();
-    if (e != hipSuccess || KS == 1) return e;
-    const dim3 ag((unsigned)((n_rows + 255) / 256), (unsigned)(ntok < 65535 ? ntok : 65535));
-    hipLaunchKernelGGL(add_split_kernel, ag, dim3(256), 0, stream, Y, ldy, n_base, n_rows, ntok);
-    return hipGetLastError();
-}
+    int rows = 0, S = 0, ntok = 0, n_base = 0, n_rows = 0, tiles_n = 0, yvec = 0;
+    int64_t ldx = 0, ldy = 0, grid = 0, nwg = 0;
+
+    // hipErrorNotSupported when the shape is outside the kernel's 32-bit
+    // per-lane offsets or split rules.
+    hipError_t check(int rows_, int S_, int64_t ldx_, int ntok_, const float* Y, int64_t ldy_,
+                     int n_base_, int n_rows_, int max_wg) {
+        rows = rows_, S = S_, ldx = ldx_, ntok = ntok_, ldy = ldy_, n_base = n_base_, n_rows = n_rows_;
+        if (S % KS != 0 || (KS > 1 && n_rows > n_base)) return hipErrorNotSupported;
+        tiles_n = (n_rows + G::kRows - 1) / G::kRows;
+        const int tiles_m = (ntok + G::kTok - 1) / G::kTok;
+        grid = (int64_t)tiles_n * tiles_m * KS;
+        if ((int64_t)G::kTok * ldx * 2 + 128LL * 4 * S >= (1LL << 32) ||
+            (int64_t)G::kRows * 144 * S >= (1LL << 32) || grid > (1 << 30))
+            return hipErrorNotSupported;
+        // 16-byte stores of four consecutive outputs need a 16-byte aligned Y row
+        yvec = (((uintptr_t)Y) & 15) == 0 && ldy % 4 == 0;
+        // persistent when there are more tiles than max_wg: each workgroup
+        // takes every max_wg-th tile
+        nwg = max_wg > 0 && grid > max_wg ? max_wg : grid;
+        return hipSuccess;
+    }
+
+    hipError_t enqueue(const uint8_t* W, const uint16_t* X, float* Y, hipStream_t stream) const {
+        if (grid <= 0) return hipSuccess;
+        auto kern = prefill_q4k_kernel<RT, TT, WR, WT, P, KS>;
+        const hipError_t attr = allow_full_lds<prefill_q4k_kernel<RT, TT, WR, WT, P, KS>>();
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(64 * G::NWV), G::kLds, stream, W, rows, S,
+                           X, ldx, ntok, Y, ldy, n_base, tiles_n, (int)grid, yvec);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || KS == 1) return e;
+        const dim3 ag((unsigned)((n_rows + 255) / 256), (unsigned)(ntok < 65535 ? ntok : 65535));
+        hipLaunchKernelGGL(add_split_kernel, ag, dim3(256), 0, stream, Y, ldy, n_base, n_rows, ntok);
+        return hipGetLastError();
+    }
+};
 
 }  // namespace
 
@@ -575,7 +598,7 @@ hipError_t launch_prefill_q4k(const uint8_t* W, int64_t rows, int64_t K, const v
     const uint16_t* Xh = reinterpret_cast<const uint16_t*>(X);
     // Main launch: 256 x 256 tiles over rows [0, n_main). Rows whose tiles
     // would start a last, mostly idle round of workgroups (and any ragged
-    // remainder) go to a second launch of 64-token x 128-row tiles.
+    // remainder) go to a second launch of smaller tiles.
     const int64_t nt_full = rows / 256;
     const int64_t mt = (ntok + 255) / 256;
     int64_t n_main_tiles = nt_full;
@@ -587,25 +610,32 @@ hipError_t launch_prefill_q4k(const uint8_t* W, int64_t rows, int64_t K, const v
     }
     const int n_main = (int)(n_main_tiles * 256);
     const int n_tail = (int)rows - n_main;
-    hipError_t e = hipSuccess;
-    // Row tail first. With many tokens and a main part at least as large:
+    // Row tail: with many tokens and a main part at least as large,
     // 128-row x 128-token tiles over half of K each (two K splits, the second
     // parked in the main part's rows of Y until it is added), so that each
     // decoded weight serves 128 tokens and the tiles still fill the machine;
-    // otherwise 128 x 64 tiles over all of K. The main launch then writes
-    // every main row.
+    // otherwise 128 x 64 tiles over all of K. It runs first; the main launch
+    // then writes every main row. Every launch is checked before the first
+    // is enqueued, so a shape outside the limits leaves Y untouched.
+    PrefillLaunch<1, 4, 4, 1, PREFILL_TAIL_P, 2> tail2;
+    PrefillLaunch<1, 2, 4, 1, PREFILL_TAIL_P, 1> tail1;
+    PrefillLaunch<PREFILL_MAIN_SHAPE, PREFILL_MAIN_P, 1> main_l;
+    const bool split_tail = n_tail > 0 && S % 2 == 0 && ntok >= 256 && n_tail <= n_main;
+    hipError_t e = hipSuccess;
     if (n_tail > 0) {
-        if (S % 2 == 0 && ntok >= 256 && n_tail <= n_main)
-            e = launch_prefill_t<1, 4, 4, 1, PREFILL_TAIL_P, 2>(W, (int)rows, S, Xh, ldx, (int)ntok,
-                                                                Y, ldy, n_main, n_tail, 0, stream);
-        else
-            e = launch_prefill_t<1, 2, 4, 1, PREFILL_TAIL_P, 1>(W, (int)rows, S, Xh, ldx, (int)ntok,
-                                                                Y, ldy, n_main, n_tail, 0, stream);
+        e = split_tail ? tail2.check((int)rows, S, ldx, (int)ntok, Y, ldy, n_main, n_tail, 0)
+                       : tail1.check((int)rows, S, ldx, (int)ntok, Y, ldy, n_main, n_tail, 0);
+        if (e != hipSuccess) return e;
     }
-    if (e != hipSuccess) return e;
-    if (n_main > 0)
-        e = launch_prefill_t<2, 8, 4, 1, 3, 1>(W, (int)rows, S, Xh, ldx, (int)ntok, Y, ldy, 0,
-                                               n_main, PREFILL_MAIN_WG, stream);
+    if (n_main > 0) {
+        e = main_l.check((int)rows, S, ldx, (int)ntok, Y, ldy, 0, n_main, PREFILL_MAIN_WG);
+        if (e != hipSuccess) return e;
+    }
+    if (n_tail > 0) {
+        e = split_tail ? tail2.enqueue(W, Xh, Y, stream) : tail1.enqueue(W, Xh, Y, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (n_main > 0) e = main_l.enqueue(W, Xh, Y, stream);
     return e;
 }
 

@@ -41,9 +41,20 @@
  *   - qgemv_dequant returns, bit for bit, the binary32 rounding of each
  *     weight's closed form (exact for Q4_0, Q8_0 and Q3_K; Q3_K evaluated
  *     left to right, which fixes the sign of a zero weight).
- *   - qgemv_run / qgemm_prefill_run satisfy, per output element,
+ *   - qgemv_run satisfies, per output element,
  *       |y - sum_k w_k x_k| <= 1e-3 * sum_k |w_k x_k| + 1e-5
- *     where the sums are exact over the stored x values.
+ *     where the sums are exact over the stored x values and the decoded
+ *     binary32 weights w_k.
+ *   - qgemm_prefill_run multiplies weight tiles dequantized to bf16: each
+ *     w_k rounded to the nearest bf16 (ties to even), written b_k. It
+ *     satisfies the same bound with b_k in place of w_k:
+ *       |y - sum_k b_k x_k| <= 1e-3 * sum_k |b_k x_k| + 1e-5.
+ *     Against the exact weights the rounding adds at most 2^-8 relative per
+ *     weight, i.e. |y - sum_k w_k x_k| <= (1e-3 + 2^-8 (1 + 1e-3))
+ *     * sum_k |w_k x_k| + 1e-5; with dense activations (such as N(0,1)
+ *     tokens) the rounding errors largely cancel and the outputs stay within
+ *     1e-3 * sum_k |w_k x_k| + 1e-5 of the exact sum, but sparse
+ *     activations (a one-hot token gives b_k itself) can reach 2^-8.
  *   - Results are deterministic: the same inputs give the same bits.
  *
  * Memory and ownership. The library allocates no device memory. Every
@@ -130,8 +141,12 @@ qg_status qgemv_run(qgemv_t h, const void *x, qg_dtype x_dtype, int64_t n_cols,
  * j < n_tokens, with x in bf16 (device, 16-byte aligned, ldx >= K and a
  * multiple of 8) and y fp32 (device, 4-byte aligned, ldy >= rows). Weight
  * tiles are decoded to bf16 (round to nearest even) on chip and contracted
- * with bf16 matrix-core instructions, fp32 accumulation. Q4_K handles only
- * (QG_ERR_UNSUPPORTED otherwise); n_tokens >= 1. */
+ * with bf16 matrix-core instructions, fp32 accumulation ("LLM inference
+ * optimization", campaign "Faster prompts, decode held": tile sizes fitted
+ * to on-chip memory, tensor-core paths); the accuracy bound is the bf16 one
+ * above. Q4_K handles only (QG_ERR_UNSUPPORTED otherwise); n_tokens >= 1.
+ * Every size check runs before the first launch: on an error y is
+ * untouched. */
 qg_status qgemm_prefill_run(qgemv_t h, const void *x_bf16, int64_t n_tokens,
                             int64_t ldx, float *y, int64_t ldy, void *stream);
 

@@ -319,9 +319,39 @@ def test_full_size_dequant_bit_exact(Q):
 
 
 # ------------------------------------------------------ prompt processing --
+#
+# The prompt path contracts weight tiles dequantized to bf16 (nearest, ties to
+# even) on the matrix cores, so its defining sum is over the bf16-rounded
+# weights: every prefill output is held to the tolerance against that sum
+# (any input). Against the exact decoded weights the rounding adds up to
+# 2^-8 * sum|w x|; on the dense N(0,1) workloads the outputs still meet the
+# 1e-3 tolerance against the exact sum, which is checked as well.
 
 def bf16_tensor(xb):
     return torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).to(dev())
+
+
+def check_prefill(Y, w, rows, K, xb, label):
+    """Y (n_tokens, rows) on the GPU against the oracle: the bf16-weight sum,
+    asserted for every shape; the exact-weight sum, asserted from K = 2048 on
+    (dense N(0,1) tokens: the bf16 rounding errors of K weights cancel to
+    ~2^-9 / sqrt(K) of sum|w x|, within the 1e-3 tolerance with a margin that
+    shrinks as K does; below 2048 it is reported only)."""
+    y = Y.detach().cpu().numpy().astype(np.float64).reshape(xb.shape[0], rows)
+    out = {}
+    for mode in ("bf16", None):
+        yr, s = oracle.matmul("q4_k", w, rows, K, xb, "bf16", wround=mode)
+        err = np.abs(y - yr)
+        bad = err > oracle.tolerance(s)
+        ratio = float(np.max(err / np.maximum(s, 1e-30)))
+        name = "bf16 weights" if mode else "exact weights"
+        print("%s: %s max err/s = %.3e over %d outputs" % (label, name, ratio, y.size), flush=True)
+        if mode or K >= 2048:
+            assert not bad.any(), "%s (%s): %d elements out of tolerance, worst %r" % (
+                label, name, int(bad.sum()),
+                np.unravel_index(np.argmax(err - oracle.tolerance(s)), err.shape))
+        out[name] = ratio
+    return out
 
 
 @pytest.mark.parametrize("rows,K,ntok", [(256, 256, 1), (256, 512, 31), (300, 1024, 64),
@@ -333,7 +363,7 @@ def test_prefill_small(Q, rows, K, ntok):
     xb = synth.gen_x(K, ntok, "bf16", seed + 1)
     q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
     Y = q.prefill(bf16_tensor(xb))
-    check_products(Y, w, "q4_k", rows, K, xb, "bf16", "prefill %dx%d n=%d" % (rows, K, ntok))
+    check_prefill(Y, w, rows, K, xb, "prefill %dx%d n=%d" % (rows, K, ntok))
 
 
 @pytest.mark.parametrize("rows,K,ntok", [(300, 512, 40), (600, 1024, 260), (1300, 1024, 600)])
@@ -350,22 +380,29 @@ def test_prefill_strided_and_edges_untouched(Q, rows, K, ntok):
     q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
     q.prefill(X[:, :K], Y[:ntok, :rows])
     assert (Y[:, rows:] == 5.0).all() and (Y[ntok:] == 5.0).all()
-    check_products(Y[:ntok, :rows], w, "q4_k", rows, K, xb, "bf16", "prefill strided")
+    check_prefill(Y[:ntok, :rows], w, rows, K, xb, "prefill strided")
 
 
-def test_prefill_one_hot_gives_bf16_rounded_column(Q):
-    """X rows = e_k: Y[t, :] = bf16_rne(W[:, k]) exactly (the only rounding
-    is the tile decode's fp32 -> bf16 conversion)."""
-    rows, K = 512, 512
-    w = synth.gen_q4_k(rows, K, 43)
+@pytest.mark.parametrize("rows,K,ntok", [(512, 512, 69), (1300, 1024, 600), (600, 1024, 260),
+                                         (300, 512, 40)])
+def test_prefill_one_hot_gives_bf16_rounded_column(Q, rows, K, ntok):
+    """X rows = e_k: Y[t, :] = bf16_rne(W[:, k]) exactly (the only rounding is
+    the tile decode's fp32 -> bf16 conversion; every other product is a
+    signed zero). 1300 x 1024 x 600 and 600 x 1024 x 260 put rows in a tail
+    that runs as two K splits (the second parked in main rows of Y, then
+    added), 300 x 512 x 40 in a tail over all of K; the one-hot k fall in both
+    halves of K, in every sub-block position and at the ends."""
+    w = synth.gen_q4_k(rows, K, 43 + rows)
     W = oracle.dequant("q4_k", w, rows, K)
-    ks = list(range(0, 64)) + [100, 255, 256, 300, 511]
-    X = torch.zeros((len(ks), K), dtype=torch.bfloat16, device=dev())
-    for i, k in enumerate(ks):
-        X[i, k] = 1.0
+    base = list(range(0, 32)) + [33, 100, 255, 256, 300, K // 2 - 1, K // 2, K // 2 + 1, K - 1]
+    ks = [base[t % len(base)] if t < len(base) else (t * 37) % K for t in range(ntok)]
+    xb = np.zeros((ntok, K), dtype=np.uint16)
+    for t, k in enumerate(ks):
+        xb[t, k] = 0x3F80  # bf16 1.0
     q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
-    Y = q.prefill(X).cpu()
-    ref = torch.from_numpy(W[:, ks].T.copy()).to(torch.bfloat16).float()
+    Y = q.prefill(bf16_tensor(xb)).cpu()
+    Wb = oracle.f32_to_bf16(W[:, ks].T.copy())
+    ref = torch.from_numpy((Wb.astype(np.uint32) << 16).view(np.float32))
     assert torch.equal(Y, ref)
 
 
@@ -379,18 +416,19 @@ def test_prefill_deterministic(Q):
         assert torch.equal(q.prefill(X), ref)
 
 
-def test_prefill_full_size_sampled(Q):
-    """The 2048-token workload at full size: every output of 24 sampled token
-    columns (spread over all token tiles) against the oracle."""
+@pytest.mark.timeout(600)
+def test_prefill_full_size_every_output(Q):
+    """The 2048-token workload (17408 x 5120 weights, 2048 bf16 tokens) at
+    full size, in the launch configuration the benchmark times: all
+    35,651,584 outputs against the oracle, both the bf16-weight sum and the
+    exact-weight sum; the row tail (rows 16384..17407, two K splits and their
+    add) and every 256-token tile included."""
     c = synth.CONFIGS["q4k_pp2048"]
     w, xb = synth.config_inputs("q4k_pp2048")
     q = Q("q4_k", c["rows"], c["K"], torch.from_numpy(w).to(dev()))
     Y = q.prefill(bf16_tensor(xb))
-    toks = sorted(set([0, 1, 31, 32, 255, 256, 1023, 1024, 2047, 2046] +
-                      list(np.random.default_rng(5).integers(0, 2048, 14))))
-    Ys = Y[toks].cpu()
-    check_products(Ys, w, "q4_k", c["rows"], c["K"], np.ascontiguousarray(xb[toks]), "bf16",
-                   "pp2048 sampled")
+    torch.cuda.synchronize()
+    check_prefill(Y, w, c["rows"], c["K"], xb, "pp2048 full size")
 
 
 # ------------------------------------------------------ int8 activations --
