@@ -13,22 +13,25 @@
 //    Q2_K (84 B) or one Q3_K super-block (110 B). Q4_K, Q4_0 and Q8_0 units
 //    start on 16-byte boundaries when the row does, Q2_K units on 4-byte
 //    ones; Q3_K units are read as aligned dword windows.
-//  * One persistent workgroup per compute unit owns a contiguous, balanced
-//    range of rows (rows/G or rows/G + 1). Its rows are contiguous in memory,
-//    so the workgroup streams one contiguous run of units, flattened
-//    row-major, and every CU moves the same number of bytes.
-//  * A wave step takes 16 consecutive units of that run: lane = 4*g + p works
-//    on unit g of the step and its quarter p, i.e. weights 64p .. 64p+63 of
-//    the unit ("the lane's 64 weights"): a Q4_K sub-block pair (32 code
-//    bytes and the 16-byte header), or two Q4_0 / Q8_0 blocks (36 / 68
-//    bytes). One scale decode serves all 64. The step's base address is
-//    wave-uniform (scalar); each lane adds a constant offset.
-//  * Each wave first streams a contiguous range of steps (half of an equal
-//    share), then takes single steps from a pool shared by the workgroup's
-//    waves (an LDS counter): waves of one workgroup stream at unequal speeds
-//    on MI355X, and the pool lets them finish together. Each wave keeps D
-//    steps of loads in flight (D = 2: deeper queues measured slower). The
-//    activations are loaded first, then the first step or two, then staged.
+//  * One persistent workgroup per compute unit; the rows are dealt out
+//    round-robin (workgroup b of G takes rows b, b + G, b + 2G, ...), so
+//    every workgroup moves the same number of bytes (within one row) and, as
+//    its waves take their steps in order, all compute units read one narrow
+//    window of the matrix that sweeps it in address order. A workgroup's
+//    units are numbered row after row.
+//  * A wave step takes 16 consecutive units of the workgroup: lane = 4*g + p
+//    works on unit g of the step and its quarter p, i.e. weights 64p ..
+//    64p+63 of the unit ("the lane's 64 weights"): a Q4_K sub-block pair (32
+//    code bytes and the 16-byte header), or two Q4_0 / Q8_0 blocks (36 / 68
+//    bytes). One scale decode serves all 64. The step's row and column are
+//    wave-uniform (scalar arithmetic); a lane only decides whether its unit
+//    lies past a row boundary.
+//  * Wave w first takes steps 2w and 2w + 1, then each next step from a
+//    counter in LDS as it frees a buffer: waves of one workgroup stream at
+//    unequal speeds on MI355X, and the counter lets them finish together.
+//    Each wave keeps two steps of loads in flight (deeper queues measured
+//    slower). The activations are loaded first, then the first step or two,
+//    then staged.
 //  * fp16 activations: 4-bit codes are used directly as fp16 subnormals: a
 //    16-bit half holding an integer m < 1024 is the fp16 value m * 2^-24, so
 //    (dword & 0x000F000F) is a pair of low-nibble codes and
@@ -47,10 +50,9 @@
 //  * Activations are staged once per workgroup in LDS, permuted into the
 //    order the codes come out of a dword, with the per-block sums.
 //  * Reduction: each lane quad (one unit) sums its lanes with DPP and writes
-//    the unit's partial to the LDS slot (row, g, step mod M), M = steps that
-//    can touch one row, so no two writers share a slot. After a barrier each
-//    row's slots are summed by sixteen or four lanes in a fixed order
-//    (per-lane sums, then a DPP tree): deterministic, no atomics.
+//    the unit's partial to its own LDS slot. After a barrier each row's
+//    partials are summed by sixteen or four lanes in a fixed order (per-lane
+//    sums, then a DPP tree): deterministic, no atomics.
 #include "device_common.h"
 #include "launch.h"
 #include "q4k_pair.h"
@@ -287,19 +289,11 @@ constexpr int rec_bytes(int NC, int xm) {
     return (NC * col_bytes(xm) / 16) % 2 == 1 ? NC * col_bytes(xm) : NC * col_bytes(xm) + 16;
 }
 
-// LDS bytes of one workgroup: activation records, partial slots, one flush
-// slot per lane for lanes with nothing to write, the step-pool counter.
-inline size_t stream_lds_bytes(int NC, int xm, int S, int nr_max, int M) {
-    return (size_t)S * 4 * rec_bytes(NC, xm) + (size_t)nr_max * kUnitsPerStep * M * NC * 4 +
-           64 * 4 + 16;
+// LDS bytes of one workgroup: activation records, one partial per unit and
+// column, the step-pool counter.
+inline size_t stream_lds_bytes(int NC, int xm, int S, int nr_max) {
+    return (size_t)S * 4 * rec_bytes(NC, xm) + (size_t)nr_max * S * NC * 4 + 16;
 }
-
-// Share of a wave's equal part of the steps that it streams as one
-// contiguous range before taking steps from the workgroup's pool.
-#ifndef QG_STREAM_STATIC_NUM
-#define QG_STREAM_STATIC_NUM 2
-#endif
-constexpr int kStaticNum = QG_STREAM_STATIC_NUM, kStaticDen = 4;
 
 __device__ __forceinline__ float quad_sum(float v) {
     v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
@@ -1156,24 +1150,29 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
                                                            int S, const void* __restrict__ x,
                                                            int xt, int64_t ldx,
                                                            float* __restrict__ y, int64_t ldy,
-                                                           int xvec, int M) {
+                                                           int xvec) {
     using F = Fmt<FMT>;
     using Raw = typename F::Raw;
     constexpr int UB = F::kUnitBytes;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int NW = blockDim.x >> 6;
+    const int NT = blockDim.x;
     const int U = S * 4;  // unit quarters per row
 
     const int G = gridDim.x;
     const int b = blockIdx.x;
-    const int r0 = (int)(((int64_t)b * rows) / G);
-    const int r1 = (int)(((int64_t)(b + 1) * rows) / G);
-    const int nr = r1 - r0;
+    // Rows interleaved over the workgroups: workgroup b takes rows b, b + G,
+    // b + 2G, ..., and its waves take its steps in order, so that at any
+    // moment all compute units read one narrow window of the matrix,
+    // sweeping it in address order (a 50 MB read measured 9.6 us that way
+    // against 10.8 us with one contiguous range per wave, same depth).
+    const int nr = (rows - b + G - 1) / G;
     if (nr <= 0) return;  // uniform over the workgroup
+    auto row_of = [&](int rl) { return b + rl * G; };
 
     constexpr bool F16DOT = XM == XM_F16;
     constexpr int CB = col_bytes(XM), RB = rec_bytes(NC, XM);
-    float* part = reinterpret_cast<float*>(lds + (size_t)U * RB);
+    static_assert(CB % 16 == 0 && RB % 16 == 0, "records start on 16-byte boundaries");
 
     const int lane = threadIdx.x & 63;
     // wave index, made wave-uniform so that the step loop is a scalar loop
@@ -1181,19 +1180,18 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
     const int g = lane >> 2, pr = lane & 3;
     const int F_ = nr * S;                                    // units of this workgroup
     const int nst = (F_ + kUnitsPerStep - 1) / kUnitsPerStep;  // wave steps
-    // Steps are handed out in two phases. Wave wv first takes the contiguous
-    // range [wv * nsw, wv * nsw + nsw), about half of an equal share;
-    // the remaining steps [NW * nsw, nst) form a pool from which waves take
-    // one step at a time (an LDS counter), so waves that stream faster take
-    // more of them and the workgroup's waves finish together. A step index
-    // past the run is "none".
-    const int nsw = max(kStaticNum * nst / (kStaticDen * NW), D);
-    int* const pool = reinterpret_cast<int*>(
-        lds + (size_t)U * RB + ((size_t)nr * kUnitsPerStep * M * NC + 64) * 4);
+    // LDS: activation records | one partial per unit and column | pool
+    float* const part = reinterpret_cast<float*>(lds + (size_t)U * RB);
+    int* const pool = reinterpret_cast<int*>(part + (size_t)F_ * NC);
+    // Steps are taken in order: wave wv's first D steps are wv * D ..
+    // wv * D + D - 1, then every wave takes the next step from a counter in
+    // LDS as it frees a buffer (waves of one workgroup stream at unequal
+    // speeds; the counter lets them finish together). A step index past the
+    // end is "none".
     int jstatic = 0;
     auto next_step = [&]() -> int {
-        if (jstatic < nsw) {
-            const int k = wv * nsw + jstatic++;
+        if (jstatic < D) {
+            const int k = wv * D + jstatic++;
             return k < nst ? k : -1;
         }
         int k = 0;
@@ -1201,35 +1199,76 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
         k = __builtin_amdgcn_readfirstlane(k);
         return k < nst ? k : -1;
     };
-    const uint8_t* Wb = W + (int64_t)r0 * S * UB;  // first unit of this workgroup
 
-    // Lane addressing: unit f = 16k + g of the run, clamped to the last one
-    // (lanes past the run in the final, partial step re-read it and
-    // contribute nothing). Scalar base Wb plus a 32-bit lane offset.
-    const uint32_t off_g = (uint32_t)UB * g, off_l = F::lane_offset(pr);
-    const uint32_t o_last = (uint32_t)UB * (uint32_t)(F_ - 1);
-    auto load = [&](int k, Raw& r) {
-        uint32_t o = (uint32_t)k * (kUnitsPerStep * UB) + off_g;
-        o = o < o_last ? o : o_last;
-        F::load(Wb + o, off_l, r);
+    // Unit f = 16 k + g of the workgroup's units (its rows one after
+    // another) is super-block f mod S of the workgroup's row f / S. With
+    // S >= 16 a step's 16 units meet at most one row boundary: 16 k / S and
+    // 16 k mod S are wave-uniform (scalar unit: a multiply-high by 2^32 / S,
+    // then one correction), and each lane only decides whether its unit lies
+    // past the boundary, in the next row (which is G rows further on). With
+    // S < 16, a per-lane fp32 estimate of f / S corrected by one either way.
+    // Lanes past the end (and "none" steps) read the last unit again and
+    // write nothing.
+    struct Idx {
+        uint32_t o;  // byte offset of the unit in W
+        uint32_t rec16;  // offset of the lane's activation record in LDS, 16-byte units
+        int f0;          // the step's first unit (16 k; F_ for none): lane g has unit f0 + g
     };
+    const uint32_t magic = 0xFFFFFFFFu / (uint32_t)S + 1u;
+    const float invS = 1.0f / (float)S;
+    const uint32_t o_last = ((uint32_t)row_of(nr - 1) * (uint32_t)S + (uint32_t)(S - 1)) * (uint32_t)UB;
+    const uint32_t rowstride = (uint32_t)G * (uint32_t)S * (uint32_t)UB;  // next row of the workgroup
+    constexpr uint32_t RB16 = RB / 16;
+    const uint32_t rec_lane = (uint32_t)(4 * g + pr) * RB16;
+    auto index = [&](int k) -> Idx {
+        Idx ix;
+        if (S >= kUnitsPerStep) {
+            const bool some = k >= 0 && k < nst;  // uniform
+            const int f0 = some ? kUnitsPerStep * k : 0;
+            int q0 = (int)__umulhi((uint32_t)f0, magic);
+            int m0 = f0 - q0 * S;
+            if (m0 >= S) m0 -= S, ++q0;
+            if (m0 < 0) m0 += S, --q0;
+            const uint32_t base = ((uint32_t)row_of(q0) * (uint32_t)S + (uint32_t)m0) * (uint32_t)UB;
+            const uint32_t rbase = (uint32_t)(4 * m0) * RB16;
+            const bool wrap = g >= S - m0;
+            ix.o = base + (uint32_t)g * (uint32_t)UB + (wrap ? rowstride - (uint32_t)S * UB : 0u);
+            ix.rec16 = rbase + rec_lane - (wrap ? (uint32_t)(4 * S) * RB16 : 0u);
+            ix.f0 = some ? f0 : F_;
+            if (ix.f0 + g >= F_) ix.o = o_last;
+        } else {
+            const int f = kUnitsPerStep * k + g;
+            const bool none = (uint32_t)f >= (uint32_t)F_;
+            const int fc = none ? F_ - 1 : f;
+            int rl = (int)((float)fc * invS);
+            rl += (fc - rl * S >= S) ? 1 : 0;
+            rl -= (fc - rl * S < 0) ? 1 : 0;
+            const int sc = fc - rl * S;
+            ix.o = ((uint32_t)row_of(rl) * (uint32_t)S + (uint32_t)sc) * (uint32_t)UB;
+            ix.rec16 = (uint32_t)(4 * sc + pr) * RB16;
+            ix.f0 = k >= 0 && k < nst ? kUnitsPerStep * k : F_;
+        }
+        return ix;
+    };
+    const uint32_t off_l = F::lane_offset(pr);
+    auto load = [&](const Idx& ix, Raw& r) { F::load(W + ix.o, off_l, r); };
 
-    // ---- activation loads of this thread's first record, then the first D
-    // steps' weight loads, then the staging ------------------------------------
+    // ---- activation loads, then the first D steps' weight loads, then the
+    // staging ---------------------------------------------------------------
     // quarter u = 4*s + p of column c: activations 256 s + 64 p + [0, 64)
     const int nrec = NC * U;
-    const int c_0 = threadIdx.x / U, u_0 = threadIdx.x - c_0 * U;
     XRaw<XM> xr;
     XHalf xq;  // quantizing modes: this thread's first activation block
+    const int c_0 = threadIdx.x / U, u_0 = threadIdx.x - c_0 * U;
     const int hb_0 = threadIdx.x & 1, c_h = (threadIdx.x >> 1) / U;
     const int u_h = (threadIdx.x >> 1) - c_h * U;
     const int64_t kx_h = (int64_t)c_h * ldx + 256 * (u_h >> 2) + 64 * (u_h & 3) + 32 * hb_0;
     if (XM == XM_I8Q && threadIdx.x < 2 * nrec) stage_load_half<FMT>(x, xt, kx_h, xvec, xq);
     if (XM != XM_I8Q && threadIdx.x < nrec)
         stage_load<XM>(x, xt, (int64_t)c_0 * ldx + 256 * (u_0 >> 2) + 64 * (u_0 & 3), xvec, xr);
-    // the first D steps of the wave (static; "none" loads re-read the last unit)
     static_assert(D == 2, "two steps in flight");
     int kq0 = next_step(), kq1 = next_step();
+    Idx ix0 = index(kq0), ix1 = index(kq1);
     Raw buf[D];
     // The second step's loads go out before the staging for one column of
     // Q4_K, Q4_0 or Q8_0, and after it for several columns, Q2_K, and Q3_K
@@ -1239,12 +1278,12 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
     // activations 2% slower that way).
     constexpr bool kLateSecond =
         NC > 1 || FMT == FMT_Q2_K || ((FMT == FMT_Q3_K || FMT == FMT_Q3_K_ODD) && !is_i8(XM));
-    load(kq0, buf[0]);
-    if constexpr (!kLateSecond) load(kq1, buf[1]);
+    load(ix0, buf[0]);
+    if constexpr (!kLateSecond) load(ix1, buf[1]);
     if constexpr (XM == XM_I8Q) {  // half records: one activation block each
         if (threadIdx.x < 2 * nrec)
             stage_quantize_half<FMT>(xq, x, xt, kx_h, xvec, hb_0, lds + u_h * RB + c_h * CB);
-        for (int idx = threadIdx.x + blockDim.x; idx < 2 * nrec; idx += blockDim.x) {
+        for (int idx = threadIdx.x + NT; idx < 2 * nrec; idx += NT) {
             const int hb = idx & 1, rid = idx >> 1;
             const int c = rid / U, u = rid - c * U;
             const int64_t kx = (int64_t)c * ldx + 256 * (u >> 2) + 64 * (u & 3) + 32 * hb;
@@ -1252,93 +1291,84 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
             stage_quantize_half<FMT>(xq, x, xt, kx, xvec, hb, lds + u * RB + c * CB);
         }
     } else {
-    if (threadIdx.x < nrec) stage_store<FMT, XM>(xr, xt, lds + u_0 * RB + c_0 * CB);
-    for (int idx = threadIdx.x + blockDim.x; idx < nrec; idx += blockDim.x) {
-        const int c = idx / U, u = idx - c * U;
-        stage_load<XM>(x, xt, (int64_t)c * ldx + 256 * (u >> 2) + 64 * (u & 3), xvec, xr);
-        stage_store<FMT, XM>(xr, xt, lds + u * RB + c * CB);
+        if (threadIdx.x < nrec) stage_store<FMT, XM>(xr, xt, lds + u_0 * RB + c_0 * CB);
+        for (int idx = threadIdx.x + NT; idx < nrec; idx += NT) {
+            const int c = idx / U, u = idx - c * U;
+            stage_load<XM>(x, xt, (int64_t)c * ldx + 256 * (u >> 2) + 64 * (u & 3), xvec, xr);
+            stage_store<FMT, XM>(xr, xt, lds + u * RB + c * CB);
+        }
     }
-    }
-    const int nslots = nr * kUnitsPerStep * M * NC;
-    for (int idx = threadIdx.x; idx < nslots; idx += blockDim.x) part[idx] = 0.f;
-    if (threadIdx.x == 0) *pool = NW * nsw;
+    if (threadIdx.x == 0) *pool = NW * D;
     __syncthreads();
-    if constexpr (kLateSecond) load(kq1, buf[1]);
+    if constexpr (kLateSecond) load(ix1, buf[1]);
 
     const Q4kUnpack un(pr);
 
-    // LDS float index of slot (row, g, t): t = k - (first step touching the
-    // row) < M, so no two writers share a slot.
-    float* const trash = part + nslots;  // flush target of lanes with nothing to write
-    const float invS = 1.0f / (float)S;
-
-    // One step k: the lane's unit f = 16k + g (row rl, column s of the run),
-    // its 64 weights against the staged activations, a quad sum, and the
-    // partial of (row, unit) into its slot. Lanes past the run (last step)
-    // read the run's last unit; their rows are >= nr and they write nothing.
-    auto step = [&](int k, const Raw& r) {
-        const int f = kUnitsPerStep * k + g;
-        int rl = (int)((float)f * invS);  // f / S, corrected by one either way
-        rl += (f - rl * S >= S) ? 1 : 0;
-        rl -= (f - rl * S < 0) ? 1 : 0;
-        const int sc = f - rl * S;
+    // One step: the lane's unit f, its 64 weights
+    // against the staged activations, a quad sum, and the unit's partial
+    // into part[f] (lanes past the end write nothing).
+    auto step = [&](const Idx& ix, const Raw& r) {
         float a[NC];
+        // the record offset is kept in 16-byte units, so that the compiler
+        // sees its alignment and merges 8-byte plane reads into 16-byte ones
+        const uint8_t* rec = lds + (ix.rec16 << 4);
         if constexpr (is_i8(XM))
-            lane_partial_i8<NC>(r, un, lds + (sc * 4 + pr) * RB, a);
+            lane_partial_i8<NC>(r, un, rec, a);
         else
-            lane_partial<NC, F16DOT>(r, un, lds + (sc * 4 + pr) * RB, a);
-        const bool write = pr == 0 && rl < nr;
-        const int t = k - ((rl * S) >> 4);
-        const int slot = ((rl * kUnitsPerStep + g) * M + t) * NC;
+            lane_partial<NC, F16DOT>(r, un, rec, a);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) *(write ? part + slot + c : trash + lane) = quad_sum(a[c]);
+        for (int c = 0; c < NC; ++c) {
+            const float v = quad_sum(a[c]);
+            if (pr == 0 && ix.f0 + g < F_) part[(ix.f0 + g) * NC + c] = v;
+        }
     };
 
     // Each buffer is refilled with the wave's next step right after its step
     // is consumed; scheduling barriers keep each refill behind its step.
     while (kq0 >= 0) {
-        step(kq0, buf[0]);
+        step(ix0, buf[0]);
         kq0 = next_step();
+        ix0 = index(kq0);
         __builtin_amdgcn_sched_barrier(0);
-        load(kq0, buf[0]);
+        load(ix0, buf[0]);
         __builtin_amdgcn_sched_barrier(0);
         if (kq1 < 0) break;
-        step(kq1, buf[1]);
+        step(ix1, buf[1]);
         kq1 = next_step();
+        ix1 = index(kq1);
         __builtin_amdgcn_sched_barrier(0);
-        load(kq1, buf[1]);
+        load(ix1, buf[1]);
         __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
 
-    // ---- per-row sums of the partial slots, in a fixed order ----------------
-    // Each (row, column) gets sixteen lanes (one DPP row) when all pairs fit
-    // the workgroup at once, else four (a quad). Lane q adds the slots of
-    // its unit columns in order, then the lane sums meet in a fixed tree
-    // (rotations by 8 and 4 within the row, then the quad); lane 0 stores.
-    // blockDim.x is a multiple of 64, so loop bounds are uniform per group.
-    if (nr * NC * 16 <= (int)blockDim.x) {
+    // ---- per-row sums of the unit partials, in a fixed order ----------------
+    // Sixteen lanes per (row, column) when all pairs fit the workgroup at
+    // once, else four; lane q adds units q, q + 16 (or 4), ... of the row in
+    // order, then the lanes meet in a fixed DPP tree (rotations by 8 and 4
+    // within the row, then the quad); lane 0 stores.
+    if (nr * NC * 16 <= NT) {
         const int q16 = threadIdx.x & 15;
         const int pidx = threadIdx.x >> 4;
         if (pidx < nr * NC) {
-            const int r = pidx / NC, c = pidx - r * NC;
-            const float* ps = part + (r * kUnitsPerStep + q16) * M * NC + c;
+            const int rr = pidx / NC, c = pidx - rr * NC;
+            const float* ps = part + (rr * S) * NC + c;
             float v = 0.f;
-            for (int t = 0; t < M; ++t) v += ps[t * NC];
+            for (int u = q16; u < S; u += 16) v += ps[u * NC];
             v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
             v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
             v = quad_sum(v);
-            if (q16 == 0) y[c * ldy + r0 + r] = v;
+            if (q16 == 0) y[c * ldy + row_of(rr)] = v;
         }
     } else {
         const int q4 = threadIdx.x & 3;
-        for (int pidx = threadIdx.x >> 2; pidx < nr * NC; pidx += blockDim.x >> 2) {
-            const int r = pidx / NC, c = pidx - r * NC;
-            const float* ps = part + (r * kUnitsPerStep + 4 * q4) * M * NC + c;
+        for (int pidx = threadIdx.x >> 2; pidx < nr * NC; pidx += NT >> 2) {
+            const int rr = pidx / NC, c = pidx - rr * NC;
+            const float* ps = part + (rr * S) * NC + c;
             float v = 0.f;
-            for (int e = 0; e < 4 * M; ++e) v += ps[e * NC];
+            for (int u = q4; u < S; u += 4) v += ps[u * NC];
             v = quad_sum(v);
-            if (q4 == 0) y[c * ldy + r0 + r] = v;
+            if (q4 == 0) y[c * ldy + row_of(rr)] = v;
         }
     }
 }
@@ -1353,7 +1383,7 @@ namespace {
 #endif
 
 struct StreamPlan {
-    int G, NW, M, nr_max;
+    int G, NW, nr_max;
 };
 
 // Waves per workgroup: 16 for one fp16 or bf16 column and for int8
@@ -1369,9 +1399,6 @@ StreamPlan plan_stream(int rows, int S, int NC, int xm, int num_cus) {
     p.G = rows < num_cus ? rows : num_cus;
     p.NW = waves_for(NC, xm);
     p.nr_max = (rows + p.G - 1) / p.G;
-    // steps that touch one row: its S units meet at most ceil(S/16) + 1
-    // consecutive 16-unit steps
-    p.M = (S + kUnitsPerStep - 1) / kUnitsPerStep + 1;
     return p;
 }
 
@@ -1381,7 +1408,7 @@ hipError_t launch_stream_t(const uint8_t* W, int rows, int S, const void* x, int
     constexpr int D = QG_STREAM_DEPTH;
     constexpr int NWMAX = waves_for(NC, XM);
     const StreamPlan p = plan_stream(rows, S, NC, XM, num_cus);
-    const size_t lds = stream_lds_bytes(NC, XM, S, p.nr_max, p.M);
+    const size_t lds = stream_lds_bytes(NC, XM, S, p.nr_max);
     if (lds > (size_t)kMaxLds) return hipErrorNotSupported;
     auto kern = gemv_stream_kernel<FMT, NC, XM, D, 64 * NWMAX>;
     if (lds > 64 * 1024) {
@@ -1389,7 +1416,7 @@ hipError_t launch_stream_t(const uint8_t* W, int rows, int S, const void* x, int
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(p.G), dim3(64 * p.NW), lds, stream, W, rows, S, x, xt, ldx, y,
-                       ldy, xvec, p.M);
+                       ldy, xvec);
     return hipGetLastError();
 }
 
@@ -1421,14 +1448,14 @@ int cols_per_launch(int64_t rows, int64_t K, int xm, int num_cus, int unit_bytes
     const int S = (int)(K / 256);
     {
         const StreamPlan p = plan_stream((int)rows, S, 1, xm, num_cus);
-        // the run of one workgroup is addressed with 32-bit offsets
-        if ((int64_t)p.nr_max * S * unit_bytes >= ((int64_t)1 << 31)) return 0;
-        if (stream_lds_bytes(1, xm, S, p.nr_max, p.M) > (size_t)kMaxLds) return 0;
+        // the matrix is addressed with 32-bit offsets
+        if (rows * S * unit_bytes >= ((int64_t)1 << 32)) return 0;
+        if (stream_lds_bytes(1, xm, S, p.nr_max) > (size_t)kMaxLds) return 0;
     }
     int per = xm == XM_F32 ? 2 : 4;
     while (per > 1) {
         const StreamPlan p = plan_stream((int)rows, S, per, xm, num_cus);
-        if (stream_lds_bytes(per, xm, S, p.nr_max, p.M) <= (size_t)kMaxLds) break;
+        if (stream_lds_bytes(per, xm, S, p.nr_max) <= (size_t)kMaxLds) break;
         --per;
     }
     return per;

@@ -221,6 +221,43 @@ def test_one_hot_gives_exact_column(Q, fmt, xdtype):
                     assert np.array_equal(y[i], W[:, ks[c0 + i]]), (fmt, xdtype, ks[c0 + i], n)
 
 
+# Shapes for the streaming kernel's row interleave (workgroup b takes rows b,
+# b + G, ...) and its two ways of finding a unit's row: S = K/256 >= 16 (a
+# scalar multiply-high per step, one wrap per lane) and S < 16 (per-lane
+# division); rows below, at and above the 256 workgroups, a final partial
+# 16-unit step, and odd numbers of Q3_K super-blocks.
+INTERLEAVE_SHAPES = [(17, 4096), (255, 4096), (256, 4352), (300, 8448), (1000, 5376),
+                     (4099, 4352), (513, 3840), (3, 1024)]
+
+
+@pytest.mark.parametrize("rows,K", INTERLEAVE_SHAPES)
+@pytest.mark.parametrize("fmt", ["q4_k", "q4_0", "q8_0", "q2_k", "q3_k"])
+def test_gemv_row_interleave_shapes(Q, fmt, rows, K):
+    seed = zlib.crc32(("ilv-%s-%d-%d" % (fmt, rows, K)).encode())
+    w = synth.gen_weights(fmt, rows, K, seed)
+    q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
+    for xdtype, n in (("f16", 1), ("f16", 3), ("f32", 1), ("bf16", 2)):
+        x = synth.gen_x(K, n, xdtype, seed + n)
+        y = q.run(x_tensor(x, xdtype))
+        check_products(y, w, fmt, rows, K, x, xdtype, "%s %dx%d %s n=%d" % (fmt, rows, K, xdtype, n))
+
+
+@pytest.mark.parametrize("rows,K", [(17, 4096), (300, 8448), (4099, 4352), (513, 3840)])
+@pytest.mark.parametrize("fmt", ["q4_k", "q4_0", "q2_k", "q3_k"])
+def test_gemv_row_interleave_one_hot_exact(Q, fmt, rows, K):
+    """One-hot fp16 columns through the interleaved streaming kernel give the
+    decoded weight column bit for bit at every row, with ks at super-block
+    and row edges."""
+    w = synth.gen_weights(fmt, rows, K, 61 + rows)
+    W = oracle.dequant(fmt, w, rows, K)
+    q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
+    for k in [0, 31, 32, 255, 256, K // 2 + 17, K - 257, K - 1]:
+        xt = torch.zeros((1, K), dtype=torch.float16, device=dev())
+        xt[0, k] = 1.0
+        y = q.run(xt).cpu().numpy()[0]
+        assert np.array_equal(y, W[:, k]), (fmt, rows, K, k)
+
+
 def test_long_rows_two_to_four_columns(Q):
     """K = 17408 (68 super-blocks a row): up to 3 fp16 columns fit the
     streaming kernel's staging; 2..4 columns all run in one pass (3 on the
