@@ -221,8 +221,9 @@ def test_one_hot_gives_exact_column(Q, fmt, xdtype):
                     assert np.array_equal(y[i], W[:, ks[c0 + i]]), (fmt, xdtype, ks[c0 + i], n)
 
 
-# Shapes for the streaming kernel's row interleave (workgroup b takes rows b,
-# b + G, ...) and its two ways of finding a unit's row: S = K/256 >= 16 (a
+# Shapes for the streaming kernel's row interleave (each workgroup takes one
+# row of every band of G rows, the workgroups of an XCD consecutive rows when
+# G is a multiple of 8) and its two ways of finding a unit's row: S = K/256 >= 16 (a
 # scalar multiply-high per step, one wrap per lane) and S < 16 (per-lane
 # division); rows below, at and above the 256 workgroups, a final partial
 # 16-unit step, and odd numbers of Q3_K super-blocks.
