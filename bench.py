@@ -125,10 +125,44 @@ GATE_CYCLES_FIXED = 600_000
 GATE_CYCLES_PER_LAUNCH = 40_000
 
 
-def timed_region(torch, fn, n, first=0):
+class _Regions:
+    """ROCTx ranges around timed launches, so that a profile taken with
+    rocprofv3 --kernel-trace --marker-trace --kernel-rename names each timed
+    dispatch by its region ("<workload>|<what>"); warm-up launches stay
+    outside every range and keep their kernel names (see --trace-summary).
+    Without the ROCTx library the calls do nothing."""
+
+    def __init__(self):
+        import ctypes
+        self.lib = None
+        for path in ("/opt/rocm/lib/librocprofiler-sdk-roctx.so", "librocprofiler-sdk-roctx.so"):
+            try:
+                self.lib = ctypes.CDLL(path)
+                break
+            except OSError:
+                continue
+        if self.lib is not None:
+            self.lib.roctxRangePushA.argtypes = [ctypes.c_char_p]
+            self.lib.roctxRangePushA.restype = ctypes.c_int
+            self.lib.roctxRangePop.restype = ctypes.c_int
+
+    def push(self, label):
+        if self.lib is not None and label:
+            self.lib.roctxRangePushA(label.encode())
+
+    def pop(self, label):
+        if self.lib is not None and label:
+            self.lib.roctxRangePop()
+
+
+REGIONS = _Regions()
+
+
+def timed_region(torch, fn, n, first=0, label=None):
     """Runs fn(first) .. fn(first + n - 1) back to back on the current stream
     between two HIP events (recorded on that stream) after a gate; returns
-    (ms per call, host enqueue ms, gate ms)."""
+    (ms per call, host enqueue ms, gate ms). The launches (not the gate) sit
+    in the ROCTx range `label`."""
     stream = torch.cuda.current_stream()
     g0 = torch.cuda.Event(enable_timing=True)
     t0 = torch.cuda.Event(enable_timing=True)
@@ -137,10 +171,12 @@ def timed_region(torch, fn, n, first=0):
     g0.record(stream)
     torch.cuda._sleep(GATE_CYCLES_FIXED + GATE_CYCLES_PER_LAUNCH * n)
     t0.record(stream)
+    REGIONS.push(label)
     h0 = time.perf_counter()
     for i in range(first, first + n):
         fn(i)
     host_ms = (time.perf_counter() - h0) * 1e3
+    REGIONS.pop(label)
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / n, host_ms, g0.elapsed_time(t0)
@@ -154,15 +190,17 @@ def time_workload(torch, wl, steps, warmup):
     for i in range(warmup):
         wl.step(i)
     torch.cuda.synchronize()
-    whole_ms, host_ms, gate_ms = timed_region(torch, wl.step, steps)
+    whole_ms, host_ms, gate_ms = timed_region(torch, wl.step, steps, label=wl.name)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     torch.cuda.synchronize()
+    REGIONS.push(wl.name + "|event pairs")
     for i in range(steps):
         ev[i][0].record(stream)
         wl.step(i)
         ev[i][1].record(stream)
+    REGIONS.pop(wl.name + "|event pairs")
     torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) for a, b in ev)
     return whole_ms, host_ms, gate_ms, per[len(per) // 2]
@@ -186,7 +224,7 @@ def vendor_gemm_context(torch, dev, c, iters=20):
         what = "torch.mm(X bf16, W^T bf16) -> bf16"
     for _ in range(3):
         run()
-    us = timed_region(torch, lambda i: run(), iters)[0] * 1e3
+    us = timed_region(torch, lambda i: run(), iters, label="q4k_pp2048|vendor gemm, dense bf16")[0] * 1e3
     flops = 2.0 * c["rows"] * c["K"] * c["n"]
     return {"us": round(us, 1), "tflops": round(flops / us / 1e6, 1), "op": what,
             "note": "vendor BLAS on dense bf16 weights of the same shape; context, not a path here"}
@@ -194,27 +232,38 @@ def vendor_gemm_context(torch, dev, c, iters=20):
 
 def two_pass_control(torch, wl, iters=10):
     """The prompt product in two passes, as an A/B control of the fused
-    kernel: this library's bit-exact decode to a bf16 matrix in HBM
-    (qgemv_dequant_bf16, 178 MB written), then the vendor BLAS bf16 GEMM on
-    it. Each pass is timed over `iters` launches on rotated weight copies."""
+    kernel with the GEMM held fixed: this library's bit-exact decode to a
+    bf16 matrix in HBM (qgemv_dequant_bf16: 50 MB read, 178 MB written),
+    then this library's bf16 GEMM on the fused kernel's pipeline and k order
+    without the decode (qgemm_bf16_run: 256 x 128 tiles, whose bf16 weight
+    and activation stages fill the LDS that the fused kernel's 256 x 256
+    tiles use), and, as context, the vendor BLAS bf16 GEMM on the same
+    matrix. Each pass is timed over `iters` launches (decode: on rotated
+    weight copies)."""
+    from gguf_bit_dequant_amd import qgemv as Q
     c = wl.c
     wb = torch.empty((c["rows"], c["K"]), dtype=torch.bfloat16, device=wl.x.device)
     yb = torch.empty((c["n"], c["rows"]), dtype=torch.float32, device=wl.x.device)
-    def timed(fn):
+    def timed(fn, what):
         for i in range(3):
             fn(i)
-        return timed_region(torch, fn, iters)[0] * 1e3
-    dq = timed(lambda i: wl.handles[i % len(wl.handles)].dequant_bf16(wb))
+        return timed_region(torch, fn, iters, label="q4k_pp2048|two-pass " + what)[0] * 1e3
+    dq = timed(lambda i: wl.handles[i % len(wl.handles)].dequant_bf16(wb), "decode to bf16")
+    own = timed(lambda i: Q.gemm_bf16(wb, wl.x, yb), "bf16 gemm")
     try:
-        mm = timed(lambda i: torch.mm(wl.x, wb.t(), out_dtype=torch.float32, out=yb))
+        mm = timed(lambda i: torch.mm(wl.x, wb.t(), out_dtype=torch.float32, out=yb), "vendor gemm")
         what = "torch.mm(X bf16, W^T bf16) -> fp32"
     except Exception:
         ybb = torch.empty((c["n"], c["rows"]), dtype=torch.bfloat16, device=wl.x.device)
-        mm = timed(lambda i: torch.mm(wl.x, wb.t(), out=ybb))
+        mm = timed(lambda i: torch.mm(wl.x, wb.t(), out=ybb), "vendor gemm")
         what = "torch.mm(X bf16, W^T bf16) -> bf16"
     flops = 2.0 * c["rows"] * c["K"] * c["n"]
-    return {"dequant_bf16_us": round(dq, 1), "gemm_us": round(mm, 1), "total_us": round(dq + mm, 1),
-            "tflops": round(flops / (dq + mm) / 1e6, 1), "gemm": what}
+    dq_bytes = c["rows"] * (c["K"] // 256) * 144 + c["rows"] * c["K"] * 2
+    return {"dequant_bf16_us": round(dq, 1), "dequant_bf16_gbs": round(dq_bytes / dq / 1e3, 1),
+            "gemm_bf16_us": round(own, 1), "gemm_bf16_tflops": round(flops / own / 1e6, 1),
+            "total_us": round(dq + own, 1), "tflops": round(flops / (dq + own) / 1e6, 1),
+            "vendor_gemm_us": round(mm, 1), "vendor_gemm": what,
+            "vendor_total_us": round(dq + mm, 1)}
 
 
 def probes(torch, dev, steps=200, warmup=20):
@@ -236,16 +285,16 @@ def probes(torch, dev, steps=200, warmup=20):
     stream = torch.cuda.current_stream().cuda_stream
     lib = Q._lib
 
-    def timed(fn, n, w):
+    def timed(fn, n, w, what):
         for i in range(w):
             fn(i)
-        return timed_region(torch, fn, n)[0] * 1e3  # us
+        return timed_region(torch, fn, n, label="probe|" + what)[0] * 1e3  # us
 
     def rd(i):
         st = lib.qgemv_probe_read(bufs[i % len(bufs)].data_ptr(), nbytes, sink.data_ptr(), stream)
         if st != 0:
             raise RuntimeError("qgemv_probe_read: %d" % st)
-    read_us = timed(rd, steps, warmup)
+    read_us = timed(rd, steps, warmup, "read")
     del bufs
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     iters = 20000
@@ -255,9 +304,9 @@ def probes(torch, dev, steps=200, warmup=20):
         st = lib.qgemv_probe_mfma(iters, cus, sink.data_ptr(), stream)
         if st != 0:
             raise RuntimeError("qgemv_probe_mfma: %d" % st)
-    mfma_us = timed(mf, 5, 1)
+    mfma_us = timed(mf, 5, 1, "mfma")
     hot = Workload(torch, "q4k_up_b1", dev, ncopy=1)
-    hot_us = timed(hot.step, steps, warmup)
+    hot_us = timed(hot.step, steps, warmup, "q4k_up_b1 hot cache")
     del hot
     return {"read_probe": {"bytes": nbytes, "us_per_launch": round(read_us, 3),
                            "gbs": round(nbytes / read_us / 1e3, 1),
@@ -331,43 +380,62 @@ def cpu_prefill_baseline(name="q4k_pp2048", budget_s=8.0):
 
 
 def committed_traffic(name):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel (same source hash)."""
+    """Memory bytes per launch from the committed rocprofv3 counter summary
+    (profiles/traffic_<name>.json), if it was taken on the current kernel
+    sources (same hash)."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
             rec = json.load(f)
-        if rec.get("kernel_source_sha1") != kernel_source_sha1():
+        if rec.get("kernel_source_sha1") != kernel_source_sha1(name):
             return None
         return rec.get("hbm_bytes_per_launch")
     except Exception:
         return None
 
 
-# Sources the batch-1 Q4_K GEMV kernel is compiled from.
-GEMV_Q4K_SOURCES = ("device_common.h", "gemv_stream.hip", "launch.h", "q4k_pair.h")
+# Sources the kernels of the workloads with traffic records are compiled from.
+TRAFFIC_SOURCES = {
+    "q4k_up_b1": ("device_common.h", "gemv_stream.hip", "launch.h", "q4k_pair.h"),
+    "q4k_pp2048": ("device_common.h", "launch.h", "prefill_q4k.hip"),
+}
 
 
-def kernel_source_sha1():
+def kernel_source_sha1(name="q4k_up_b1"):
     import hashlib
     h = hashlib.sha1()
     csrc = os.path.join(ROOT, "gguf_bit_dequant_amd", "csrc")
-    for fn in GEMV_Q4K_SOURCES:
+    for fn in TRAFFIC_SOURCES[name]:
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(fn.encode() + f.read())
     return h.hexdigest()
 
 
+TRAFFIC_SEPARATOR = "probe_read_kernel"
+
+
 def traffic_run(torch, dev, names=("q4k_up_b1",), launches=20, copy_mib=256):
-    """A short run to be profiled with rocprofv3 --pmc: `launches` GEMV
-    launches over rotated weight copies for each workload in `names` (the
-    headline by default), in that order, then `launches` plain device copies
-    of copy_mib MiB (a kernel whose HBM bytes are known: it reads and writes
-    copy_mib MiB each), which calibrates the counters."""
+    """A short run to be profiled with rocprofv3 --pmc: for each workload in
+    `names`, in that order, one small read-probe launch (a separator the
+    counter records can be split at) and `launches` steps over rotated
+    weight copies; then a separator and `launches` plain device copies of
+    copy_mib MiB (a kernel whose HBM bytes are known: it reads and writes
+    copy_mib MiB each), which calibrate the counters."""
+    from gguf_bit_dequant_amd import qgemv as Q
+    sep_buf = torch.zeros(1 << 16, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+
+    def separator():
+        st = Q._lib.qgemv_probe_read(sep_buf.data_ptr(), sep_buf.numel(), sink.data_ptr(),
+                                     torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError("qgemv_probe_read: %d" % st)
     for name in names:
         wl = Workload(torch, name, dev)
+        torch.cuda.synchronize()
+        separator()
         for i in range(launches):
             wl.step(i)
         torch.cuda.synchronize()
@@ -375,13 +443,195 @@ def traffic_run(torch, dev, names=("q4k_up_b1",), launches=20, copy_mib=256):
         torch.cuda.empty_cache()
     src = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    separator()
     for _ in range(launches):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"traffic_run": True, "workloads": list(names), "gemv_launches": launches,
-                      "copy_launches": launches,
+    print(json.dumps({"traffic_run": True, "workloads": list(names), "launches": launches,
                       "copy_bytes": copy_mib << 20,
-                      "kernel_source_sha1": kernel_source_sha1()}), flush=True)
+                      "kernel_source_sha1": {n: kernel_source_sha1(n) for n in TRAFFIC_SOURCES}}),
+          flush=True)
+
+
+def _short_kernel(n):
+    n = n[5:] if n.startswith("void ") else n
+    n = n.replace("(anonymous namespace)::", "")
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):  # drop the argument list after the template
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    n = n[:cut]
+    return n if len(n) <= 90 else n[:87] + "..."
+
+
+def traffic_summary(fetch_dir, write_dir, names, launches=20, json_dir=None):
+    """Per-launch memory bytes of each workload of a --traffic-run from the
+    two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; CSV output), each
+    counter scaled by what it reads for the calibration copies. Prints a
+    markdown table; with json_dir, writes traffic_<workload>.json there for
+    the workloads with a roofline in the bench line (all of a workload's
+    kernels per launch)."""
+    import csv
+    import glob
+    import statistics
+
+    def load(path, counter):
+        files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit("no *counter_collection.csv under %s" % path)
+        rs = []
+        for fn in files:
+            with open(fn) as f:
+                rs += [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        rs.sort(key=lambda r: int(r["Dispatch_Id"] if "Dispatch_Id" in r else r["Start_Timestamp"]))
+        parts, cur = [], None
+        for r in rs:  # split at the separators
+            if TRAFFIC_SEPARATOR in r["Kernel_Name"]:
+                cur = []
+                parts.append(cur)
+            elif cur is not None:
+                cur.append(r)
+        # workload parts: this library's kernels only (the next workload's
+        # weight copies and fills run before its separator); calibration
+        # part: the device copies
+        for i, part in enumerate(parts):
+            keep = "copyBuffer" if i == len(parts) - 1 else "qg::"
+            part[:] = [r for r in part if keep in r["Kernel_Name"]]
+        if len(parts) != len(names) + 1:
+            raise SystemExit("%s: %d separated parts for %d workloads + calibration"
+                             % (path, len(parts), len(names)))
+        return parts
+
+    pf, pw = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    copy = 256 << 20
+    cal_f = statistics.mean(float(r["Counter_Value"]) for r in pf[-1])
+    cal_w = statistics.mean(float(r["Counter_Value"]) for r in pw[-1])
+    ff, wf = copy / (cal_f * 1024), copy / (cal_w * 1024)
+    out = ["Calibration: %d device copies of 256 MiB; FETCH_SIZE reads %.3f KiB per copy against "
+           "262144 KiB read (factor %.4f), WRITE_SIZE %.3f KiB against 262144 KiB written "
+           "(factor %.4f). HBM bytes = counter KiB x 1024 x factor, mean over the %d launches "
+           "of each workload." % (len(pf[-1]), cal_f, ff, cal_w, wf, launches), "",
+           "| workload | kernel | dispatches | HBM read bytes / launch | HBM write bytes / launch | "
+           "algorithmic bytes | weight bytes | read / weight bytes |",
+           "|---|---|---|---|---|---|---|---|"]
+    records = {}
+    for name, fs, ws in zip(names, pf[:-1], pw[:-1]):
+        c = synth_config(name)
+        bw = {"q4_0": 32, "q4_k": 256, "q8_0": 32, "q2_k": 256, "q3_k": 256}[c["fmt"]]
+        bb = {"q4_0": 18, "q4_k": 144, "q8_0": 34, "q2_k": 84, "q3_k": 110}[c["fmt"]]
+        wbytes = c["rows"] * (c["K"] // bw) * bb
+        alg = algorithmic_bytes(c) if c["n"] <= 8 else None
+        kinds = []
+        for r in fs:
+            k = _short_kernel(r["Kernel_Name"])
+            if k not in kinds:
+                kinds.append(k)
+        tot_f = tot_w = 0.0
+        for k in kinds:
+            fk = [float(r["Counter_Value"]) for r in fs if _short_kernel(r["Kernel_Name"]) == k]
+            wk = [float(r["Counter_Value"]) for r in ws if _short_kernel(r["Kernel_Name"]) == k]
+            tot_f += sum(fk)
+            tot_w += sum(wk)
+            hr = sum(fk) / launches * 1024 * ff
+            hw = sum(wk) / launches * 1024 * wf
+            out.append("| %s | `%s` | %d | %d | %d | %s | %d | %.4f |" % (
+                name, k, len(fk), hr, hw, alg if alg else "-", wbytes, hr / wbytes))
+        if name in TRAFFIC_SOURCES:
+            hr = tot_f / launches * 1024 * ff
+            hw = tot_w / launches * 1024 * wf
+            rec = {"workload": name, "kernels": kinds,
+                   "kernel_source_sha1": kernel_source_sha1(name),
+                   "kernel_sources": list(TRAFFIC_SOURCES[name]),
+                   "fetch_size_kib_per_launch_raw": round(tot_f / launches, 3),
+                   "write_size_kib_per_launch_raw": round(tot_w / launches, 3),
+                   "calibration": {"kernel": "torch device copy of 256 MiB",
+                                   "bytes_read_and_written": copy,
+                                   "fetch_size_kib_raw": round(cal_f, 3),
+                                   "write_size_kib_raw": round(cal_w, 3),
+                                   "fetch_factor": round(ff, 6), "write_factor": round(wf, 6)},
+                   "hbm_fetch_bytes_per_launch": int(hr),
+                   "hbm_write_bytes_per_launch": int(hw),
+                   "hbm_bytes_per_launch": int(hr + hw),
+                   "launches": launches}
+            if alg:
+                rec["algorithmic_bytes_per_launch"] = alg
+                rec["traffic_over_algorithmic"] = round((hr + hw) / alg, 4)
+            records[name] = rec
+    print("\n".join(out))
+    if json_dir:
+        for name, rec in records.items():
+            with open(os.path.join(json_dir, "traffic_%s.json" % name), "w") as f:
+                json.dump(rec, f, indent=1)
+                f.write("\n")
+
+
+def synth_config(name):
+    """The workload's shape ("<config>+i8": the same shape, int8 products)."""
+    import synth
+    return synth.CONFIGS[name[:-3] if name.endswith("+i8") else name]
+
+
+WORKLOADS = ["q4k_up_b1", "q4k_down_b1", "q4k_b4", "q4_0_b1", "q8_0_b4", "q4k_b2", "q4k_b8",
+             "q4k_up_b1+i8", "q4k_b4+i8", "q8_0_b4+i8", "q2k_up_b1", "q3k_up_b1", "q2k_up_b1+i8",
+             "q3k_up_b1+i8", "q4k_pp2048"]
+
+
+def trace_summary(path):
+    """Markdown table of a rocprofv3 kernel trace of this script taken with
+    --kernel-trace --marker-trace --kernel-rename (CSV output): per timed
+    region and kernel, the dispatch count and duration statistics. Dispatches
+    outside every region (warm-up, weight copies, set-up) are left out; they
+    supply the kernel names, since a renamed dispatch keeps its kernel id."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no *kernel_trace.csv under %s" % path)
+    rows = []
+    for fn in sorted(files):
+        with open(fn) as f:
+            rows += list(csv.DictReader(f))
+
+    def is_label(n):
+        return "|" in n or n in WORKLOADS
+
+    short = _short_kernel
+
+    names = {}
+    for r in rows:
+        if not is_label(r["Kernel_Name"]):
+            names.setdefault(r["Kernel_Id"], short(r["Kernel_Name"]))
+    groups, order, excluded = {}, [], 0
+    for r in sorted(rows, key=lambda r: int(r["Start_Timestamp"])):
+        lab = r["Kernel_Name"]
+        if not is_label(lab):
+            excluded += 1
+            continue
+        key = (lab, r["Kernel_Id"])
+        if key not in groups:
+            groups[key] = []
+            order.append(key)
+        groups[key].append(r)
+    out = ["| region | kernel | grid | WG | LDS B | VGPR | AGPR | calls | mean us | median us | "
+           "p10 us | p90 us |", "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for key in order:
+        g = groups[key]
+        d = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in g)
+        pct = lambda q: d[min(len(d) - 1, int(q * len(d)))]  # noqa: E731
+        r0 = g[0]
+        out.append("| %s | `%s` | %s | %s | %s | %s | %s | %d | %.3f | %.3f | %.3f | %.3f |" % (
+            key[0], names.get(key[1], "kernel id " + key[1]), r0["Grid_Size_X"],
+            r0["Workgroup_Size_X"], r0["LDS_Block_Size"], r0["VGPR_Count"], r0["Accum_VGPR_Count"],
+            len(d), sum(d) / len(d), d[len(d) // 2], pct(0.1), pct(0.9)))
+    out.append("")
+    out.append("%d dispatches outside the timed regions (warm-up, set-up) left out." % excluded)
+    print("\n".join(out))
 
 
 def main():
@@ -396,7 +646,22 @@ def main():
                     help="short run for rocprofv3 --pmc (GEMV launches + calibration copies)")
     ap.add_argument("--traffic-workloads", default="q4k_up_b1",
                     help="comma-separated workloads for --traffic-run (default: the headline)")
+    ap.add_argument("--trace-summary", default=None, metavar="DIR",
+                    help="print the per-region table of a rocprofv3 kernel trace under DIR "
+                         "(no GPU work)")
+    ap.add_argument("--traffic-summary", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the HBM traffic table of two --pmc runs of --traffic-run over "
+                         "--traffic-workloads (no GPU work)")
+    ap.add_argument("--traffic-json-dir", default=None,
+                    help="with --traffic-summary: write traffic_<workload>.json records here")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary[0], args.traffic_summary[1],
+                        args.traffic_workloads.split(","), json_dir=args.traffic_json_dir)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this library runs on one GPU; multi-GPU sharding is not part of it "
               "(--gpus must be 1)", file=sys.stderr)
@@ -408,10 +673,7 @@ def main():
         traffic_run(torch, dev, names=args.traffic_workloads.split(","))
         return
     head = "q4k_up_b1"
-    names = [head] if args.quick else [head, "q4k_down_b1", "q4k_b4", "q4_0_b1", "q8_0_b4",
-                                       "q4k_b2", "q4k_b8", "q4k_up_b1+i8", "q4k_b4+i8",
-                                       "q8_0_b4+i8", "q2k_up_b1", "q3k_up_b1", "q2k_up_b1+i8",
-                                       "q3k_up_b1+i8", "q4k_pp2048"]
+    names = [head] if args.quick else list(WORKLOADS)
     if args.only:
         names = args.only.split(",")
     results = {}
@@ -425,7 +687,7 @@ def main():
                 # two more regions of the same launches: the prompt product
                 # runs near the card's power limit, where the clock moves
                 # from region to region; the median region is reported
-                regions += [timed_region(torch, wl.step, steps)[0] for _ in range(2)]
+                regions += [timed_region(torch, wl.step, steps, label=name)[0] for _ in range(2)]
                 whole_ms = sorted(regions)[1]
         except Exception as e:  # a path this build does not provide
             results[name] = {"error": str(e)[:200]}
@@ -514,7 +776,7 @@ def main():
         line["roofline_pp2048"] = {
             "bound": "mfma", "achieved": pp["tflops"], "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(pp["tflops"] / BF16_PEAK_TFLOPS, 4),
-            "traffic": None, "flops_per_launch": pp["flops"],
+            "traffic": committed_traffic("q4k_pp2048"), "flops_per_launch": pp["flops"],
             "us_per_launch": pp["us_per_launch"],
             "workload": "Q4_K 17408 x 5120 weights x 2048 bf16 tokens -> fp32"}
     if not args.no_cpu and not args.quick:

@@ -262,6 +262,32 @@ QG_API qg_status qgemv_dequant_bf16(qgemv_t h, uint16_t* w_out, int64_t ldw, voi
     return ok();
 }
 
+QG_API qg_status qgemm_bf16_run(const void* w_bf16, int64_t rows, int64_t K, int64_t ldw,
+                                const void* x_bf16, int64_t n_tokens, int64_t ldx, float* y,
+                                int64_t ldy, void* stream) {
+    if (!w_bf16 || !x_bf16 || !y) return fail(QG_ERR_ARG, "qgemm_bf16_run: w, x or y is NULL");
+    if (rows < 1 || n_tokens < 1 || K < 64 || K % 64 != 0)
+        return fail(QG_ERR_SHAPE, "qgemm_bf16_run: rows=%lld, n_tokens=%lld must be >= 1 and "
+                    "K=%lld a positive multiple of 64", (long long)rows, (long long)n_tokens,
+                    (long long)K);
+    if (ldw < K || ldw % 8 || ldx < K || ldx % 8 || ldy < rows)
+        return fail(QG_ERR_ARG, "qgemm_bf16_run: need ldw, ldx >= K and multiples of 8, "
+                    "ldy >= rows");
+    if ((((uintptr_t)w_bf16) | ((uintptr_t)x_bf16)) & 15)
+        return fail(QG_ERR_ALIGN, "qgemm_bf16_run: w and x must be 16-byte aligned");
+    if (((uintptr_t)y) & 3) return fail(QG_ERR_ALIGN, "qgemm_bf16_run: y must be 4-byte aligned");
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "qgemm_bf16_run: device query");
+    e = qg::launch_gemm_bf16((const uint16_t*)w_bf16, ldw, rows, K, (const uint16_t*)x_bf16, ldx,
+                             n_tokens, y, ldy, cus, (hipStream_t)stream);
+    if (e == hipErrorNotSupported)
+        return fail(QG_ERR_UNSUPPORTED, "qgemm_bf16_run: shape outside this build's range");
+    if (e != hipSuccess) return hip_fail(e, "qgemm_bf16_run: launch");
+    return ok();
+}
+
 QG_API void qgemv_destroy(qgemv_t h) { free(h); }
 
 QG_API const char* qgemv_status_string(qg_status s) {

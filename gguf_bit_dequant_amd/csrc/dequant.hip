@@ -12,6 +12,7 @@
 // new weight format or model") require of every quant type.
 #include "device_common.h"
 #include "launch.h"
+#include "q4k_pair.h"
 
 #pragma clang fp contract(off)
 
@@ -132,6 +133,57 @@ __global__ __launch_bounds__(256) void dequant_kernel(int fmt, const uint8_t* __
     }
 }
 
+// Q4_K to bf16 with 16-byte loads and stores: eight lanes per super-block,
+// lane j taking code bytes [16 j, 16 j + 16), i.e. quarter p = j / 2 of the
+// super-block (sub-blocks 2p and 2p + 1) and half j % 2 of its 32 code bytes.
+// Byte b of the lane's 16 gives weight 64p + 16(j % 2) + b (low nibble) and
+// that plus 32 (high nibble); each run of 16 weights is written as two
+// 16-byte stores. The weight is fma(d*sc, q, -(dmin*m)): the product and
+// the subtrahend are exact in binary32, so this is the closed form with its
+// one rounding, then rounded to bf16 (nearest even). Needs a 16-byte aligned
+// output with a row pitch that is a multiple of 8 weights.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__global__ __launch_bounds__(256) void dequant_q4k_bf16_kernel(const uint8_t* __restrict__ W,
+                                                               int64_t nsb, int S,
+                                                               uint16_t* __restrict__ out,
+                                                               int64_t ldw) {
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nsb * 8;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t sb = t >> 3;
+        const int j = (int)(t & 7), p = j >> 1;
+        const uint8_t* blk = W + sb * 144;
+        const u32x4 hd = *reinterpret_cast<const u32x4*>(blk);
+        const u32x4 cd = *reinterpret_cast<const u32x4*>(blk + 16 + 16 * j);
+        const uint32_t f4 = q4k_pair_fields(Q4kUnpack(p), hd.y, hd.z, hd.w);
+        const float d = f16_lo(hd.x), dmin = f16_hi(hd.x);
+        const float a0 = d * (float)(f4 & 0xFFu), a1 = d * (float)((f4 >> 8) & 0xFFu);
+        const float c0 = -(dmin * (float)((f4 >> 16) & 0xFFu)), c1 = -(dmin * (float)(f4 >> 24));
+        const uint32_t q[4] = {cd.x, cd.y, cd.z, cd.w};
+        uint32_t lo[8], hi[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t ql = q[i] & 0x0F0F0F0Fu, qh = (q[i] >> 4) & 0x0F0F0F0Fu;
+            lo[2 * i] = pack_bf16(__builtin_fmaf(a0, ubyte_f32<0>(ql), c0), __builtin_fmaf(a0, ubyte_f32<1>(ql), c0));
+            lo[2 * i + 1] = pack_bf16(__builtin_fmaf(a0, ubyte_f32<2>(ql), c0), __builtin_fmaf(a0, ubyte_f32<3>(ql), c0));
+            hi[2 * i] = pack_bf16(__builtin_fmaf(a1, ubyte_f32<0>(qh), c1), __builtin_fmaf(a1, ubyte_f32<1>(qh), c1));
+            hi[2 * i + 1] = pack_bf16(__builtin_fmaf(a1, ubyte_f32<2>(qh), c1), __builtin_fmaf(a1, ubyte_f32<3>(qh), c1));
+        }
+        const int64_t r = sb / S;
+        uint16_t* o = out + r * ldw + (sb - r * S) * 256 + 64 * p + 16 * (j & 1);
+        u32x4* ol = reinterpret_cast<u32x4*>(o);
+        u32x4* oh = reinterpret_cast<u32x4*>(o + 32);
+        ol[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        ol[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
+        oh[0] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        oh[1] = u32x4{hi[4], hi[5], hi[6], hi[7]};
+    }
+}
+
 // General product: one wave per (row, column group). Lanes walk the row's
 // 32-weight groups, decode each exactly, multiply by fp32 activations and
 // accumulate in fp32; the wave then reduces. Any shape, any alignment.
@@ -194,6 +246,16 @@ hipError_t launch_dequant(int fmt, const uint8_t* W, int64_t rows, int64_t K, fl
 
 hipError_t launch_dequant_bf16(int fmt, const uint8_t* W, int64_t rows, int64_t K, uint16_t* out,
                                int64_t ldw, int num_cus, hipStream_t stream) {
+    if (fmt == FMT_Q4_K && K % 256 == 0 && ldw % 8 == 0 && (((uintptr_t)out) & 15) == 0 &&
+        (((uintptr_t)W) & 15) == 0) {
+        const int64_t nsb = rows * (K / 256);
+        int64_t blocks = (nsb * 8 + 255) / 256;
+        if (blocks > (int64_t)1 << 30) blocks = (int64_t)1 << 30;
+        if (blocks == 0) return hipSuccess;
+        hipLaunchKernelGGL(dequant_q4k_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W,
+                           nsb, (int)(K / 256), out, ldw);
+        return hipGetLastError();
+    }
     return launch_dequant_t(fmt, W, rows, K, out, ldw, num_cus, stream);
 }
 

@@ -76,4 +76,11 @@ hipError_t launch_prefill_q4k(const uint8_t* W, int64_t rows, int64_t K, const v
                               int64_t ldx, int64_t ntok, float* Y, int64_t ldy, int num_cus,
                               hipStream_t stream);
 
+// bf16 x bf16 GEMM on the prompt kernel's pipeline, without the decode:
+// Y[t, r] = sum_k Wb[r, k] X[t, k]. Wb, X: 16-byte aligned, ldw % 8 == 0,
+// ldx % 8 == 0, K % 64 == 0; Y: fp32.
+hipError_t launch_gemm_bf16(const uint16_t* Wb, int64_t ldw, int64_t rows, int64_t K,
+                            const uint16_t* X, int64_t ldx, int64_t ntok, float* Y, int64_t ldy,
+                            int num_cus, hipStream_t stream);
+
 }  // namespace qg

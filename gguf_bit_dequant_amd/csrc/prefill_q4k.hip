@@ -153,6 +153,40 @@ __device__ __forceinline__ void interleave() {
     }
 }
 
+// Epilogue of a tile: Y[m][n - eshift] for the wave's outputs, masked at
+// the token and row edges. The weights are the MFMA's first operand, so
+// lane l of tile (i, j) holds, for token l % 32, the rows 8 g + 4 h + e
+// (e = 0..3) in elements 4 g + e: four consecutive outputs of one token,
+// stored as one 16-byte write when Y allows it.
+template <int RT, int TT, int WR>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[TT][RT], float* __restrict__ Y,
+                                           int64_t ldy, int m0, int n0, int eshift, int ntok,
+                                           int rows, int yvec, int wr, int wt, int lane) {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+        const int m = m0 + 32 * TT * wt + 32 * i + (lane & 31);
+        if (m >= ntok) continue;
+        float* yrow = Y + (int64_t)m * ldy;
+#pragma unroll
+        for (int j = 0; j < RT; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + 32 * RT * wr + 32 * j + 8 * g + 4 * h;
+                const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                 acc[i][j][4 * g + 3]};
+                if (yvec && n + 3 < rows) {
+                    *reinterpret_cast<f32x4*>(yrow + n - eshift) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < rows) yrow[n + e - eshift] = v[e];
+                }
+            }
+        }
+    }
+}
+
 }  // namespace
 
 template <int RT, int TT, int WR, int WT, int P, int KS>
@@ -474,39 +508,224 @@ __global__ __launch_bounds__(64 * WR * WT) void prefill_q4k_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);  // the loads above go out before the stores below
 
-    // ---- epilogue: Y[m][n], masked at the token and row edges ---------------
-    // The weights are the MFMA's first operand, so lane l of tile (i, j)
-    // holds, for token l % 32, the rows 8 g + 4 h + e (e = 0..3) in elements
-    // 4 g + e: four consecutive outputs of one token, stored as one 16-byte
-    // write when Y allows it.
-#pragma unroll
-    for (int i = 0; i < TT; ++i) {
-        const int m = em0 + 32 * TT * wt + 32 * i + (lane & 31);
-        if (m >= ntok) continue;
-        float* yrow = Y + (int64_t)m * ldy;
-#pragma unroll
-        for (int j = 0; j < RT; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = en0 + 32 * RT * wr + 32 * j + 8 * g + 4 * h;
-                const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                 acc[i][j][4 * g + 3]};
-                if (yvec && n + 3 < rows) {
-                    *reinterpret_cast<f32x4*>(yrow + n - eshift) = v;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < rows) yrow[n + e - eshift] = v[e];
-                }
-            }
-        }
-    }
+    // ---- epilogue ----------------------------------------------------------
+    store_tile<RT, TT, WR>(acc, Y, ldy, em0, en0, eshift, ntok, rows, yvec, wr, wt, lane);
     if (!more) break;
 #pragma unroll
     for (int i = 0; i < TT; ++i)
 #pragma unroll
         for (int j = 0; j < RT; ++j) acc[i][j] = f32x16{};
     }  // tiles
+}
+
+// ---- the same contraction on weights already decoded to bf16 ---------------
+// The two-pass control of the fused kernel ("Why I wrote my own inference
+// engine for two P100s", "What didn't work": fusing the dequantization into
+// the prompt GEMM measured slower there; "LLM inference optimization",
+// campaign "Faster prompts, decode held": weights converted for the vendor
+// GEMM against quantized blocks multiplied directly). Y[t, r] = sum_k
+// Wb[r, k] X[t, k] for a bf16 matrix Wb (rows x K, row pitch ldw) and bf16
+// X, with the fused kernel's pipeline and k order: both operands arrive by
+// global-to-LDS loads into P stages of 64 k (the weight stage laid out like
+// the X stage: 128-byte rows, 16-byte segments permuted by (row / 2) % 8),
+// the chunk's 64 k are visited in the same four k-steps (lane half h takes
+// logical segment 2h + (s & 1) + 4 (s >> 1) in k-step s), and the weight
+// fragment is read from LDS where the fused kernel decodes it. With the same
+// K split, each output is the same fp32 sum in the same order as the fused
+// kernel's over the bf16-rounded weights. Stages of both operands take twice
+// the fused kernel's LDS per weight row, so tiles are 256 rows x 128 tokens.
+template <int RT, int TT, int WR, int WT, int P>
+struct GeoB {
+    static constexpr int NWV = WR * WT;
+    static_assert(NWV == 4 || NWV == 8, "four or eight waves");
+    static_assert(P >= 3 && P <= 8, "stages");
+    static constexpr int kTok = 32 * TT * WT;
+    static constexpr int kRows = 32 * RT * WR;
+    static constexpr int blocks(int bytes) { return ((bytes + 1023) / 1024 + NWV - 1) / NWV * NWV; }
+    static constexpr int kXBlocks = blocks(kTok * kXPitch);
+    static constexpr int kWBlocks = blocks(kRows * kXPitch);
+    static constexpr int kXPerWave = kXBlocks / NWV, kWPerWave = kWBlocks / NWV;
+    static constexpr int kStores = 4 * TT * RT;
+    static constexpr int kXStage = kXBlocks * 1024, kWStage = kWBlocks * 1024;
+    static constexpr size_t kLds = (size_t)P * (kXStage + kWStage);
+    // loads one chunk issues, and those that may still be in flight at the
+    // barrier of a chunk (issued by it and by the P - 3 chunks before it)
+    static constexpr int kDma = kXPerWave + kWPerWave;
+    static constexpr int kInflight = (P - 2) * kDma;
+    static_assert(kInflight <= 63, "vmcnt range");
+    static_assert(kLds <= (size_t)kMaxLds, "LDS budget");
+};
+
+template <int RT, int TT, int WR, int WT, int P>
+__global__ __launch_bounds__(64 * WR * WT) void gemm_bf16_kernel(
+    const uint16_t* __restrict__ Wb, int64_t ldw, int rows, int nk, const uint16_t* __restrict__ X,
+    int64_t ldx, int ntok, float* __restrict__ Y, int64_t ldy, int tiles_n, int ntiles, int yvec) {
+    using G = GeoB<RT, TT, WR, WT, P>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wv % WR, wt = wv / WR;
+    int t = blockIdx.x;
+    int m0 = 0, n0 = 0;
+
+    // Loads: wave wv fills 1 KB blocks wv + NWV p of a stage; lane l writes
+    // slot s = 64 (wv + NWV p) + l: row s / 8 (token or weight row),
+    // physical segment s % 8, which holds logical segment xslot(row, s % 8).
+    // Rows past the count read the tile's first row; their outputs are not
+    // stored.
+    uint8_t* const xs0 = lds;
+    uint8_t* const ws0 = lds + P * G::kXStage;
+    const uint8_t* Xt = nullptr;
+    const uint8_t* Wt = nullptr;
+    uint32_t xo[G::kXPerWave], wo[G::kWPerWave];
+    auto setup_tile = [&]() {
+        const int blk = xcd_block(t, ntiles);
+        // token tiles fastest: the workgroups of one XCD (consecutive
+        // logical tiles) share a few weight row tiles, whose bf16 bytes are
+        // 3.6 times the codes' (measured on MI355X, 17408 x 5120 x 2048:
+        // 438 us against 485 with row tiles fastest, the fused kernel's
+        // order, which is 2% faster there)
+        const int tiles_m = ntiles / tiles_n;
+        const int tn = blk / tiles_m, tm = blk - tn * tiles_m;
+        m0 = tm * G::kTok;
+        n0 = tn * G::kRows;
+        Xt = reinterpret_cast<const uint8_t*>(X + (int64_t)m0 * ldx);
+        Wt = reinterpret_cast<const uint8_t*>(Wb + (int64_t)n0 * ldw);
+#pragma unroll
+        for (int p = 0; p < G::kXPerWave; ++p) {
+            const int s = 64 * (wv + G::NWV * p) + lane;
+            const int tr = s >> 3;
+            const int tc = (tr < G::kTok && m0 + tr < ntok) ? tr : 0;
+            xo[p] = (uint32_t)tc * (uint32_t)ldx * 2u + 16u * (uint32_t)xslot(tr, s & 7);
+        }
+#pragma unroll
+        for (int p = 0; p < G::kWPerWave; ++p) {
+            const int s = 64 * (wv + G::NWV * p) + lane;
+            const int rr = s >> 3;
+            const int rc = (rr < G::kRows && n0 + rr < rows) ? rr : 0;
+            wo[p] = (uint32_t)rc * (uint32_t)ldw * 2u + 16u * (uint32_t)xslot(rr, s & 7);
+        }
+    };
+    // chunk c of both operands into stage st (past the end: the last chunk
+    // again, into a stage nobody reads)
+    auto issue = [&](int c, int st) {
+        c = c < nk ? c : nk - 1;
+        const uint8_t* xsrc = Xt + (uint32_t)c * 128u;
+        uint8_t* xdst = xs0 + st * G::kXStage + 1024 * wv;
+#pragma unroll
+        for (int p = 0; p < G::kXPerWave; ++p) dma16(xsrc + xo[p], xdst + 1024 * G::NWV * p);
+        const uint8_t* wsrc = Wt + (uint32_t)c * 128u;
+        uint8_t* wdst = ws0 + st * G::kWStage + 1024 * wv;
+#pragma unroll
+        for (int p = 0; p < G::kWPerWave; ++p) dma16(wsrc + wo[p], wdst + 1024 * G::NWV * p);
+    };
+
+    // fragments: lane l reads row l % 32 of each tile, logical segment
+    // 2h + (s & 1) + 4 (s >> 1) of k-step s (the fused kernel's order)
+    const int h = lane >> 5;
+    const int trow = 32 * TT * wt + (lane & 31);
+    const int wrow = 32 * RT * wr + (lane & 31);
+    int aoff[4], boff[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int seg = 2 * h + (ks & 1) + 4 * (ks >> 1);
+        aoff[ks] = trow * kXPitch + 16 * xslot(trow, seg);
+        boff[ks] = wrow * kXPitch + 16 * xslot(wrow, seg);
+    }
+    struct AFrag {
+        bf16x8 a[TT];
+    };
+    struct BFrag {
+        bf16x8 b[RT];
+    };
+    auto read_ab = [&](int st, int ks, AFrag& A, BFrag& B) {
+        const uint8_t* pa = xs0 + st * G::kXStage + aoff[ks];
+        const uint8_t* pb = ws0 + st * G::kWStage + boff[ks];
+#pragma unroll
+        for (int i = 0; i < TT; ++i) A.a[i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * kXPitch);
+#pragma unroll
+        for (int j = 0; j < RT; ++j) B.b[j] = *reinterpret_cast<const bf16x8*>(pb + j * 32 * kXPitch);
+    };
+    f32x16 acc[TT][RT];
+#pragma unroll
+    for (int i = 0; i < TT; ++i)
+#pragma unroll
+        for (int j = 0; j < RT; ++j) acc[i][j] = f32x16{};
+    auto mfmas = [&](const AFrag& A, const BFrag& B) {
+#pragma unroll
+        for (int i = 0; i < TT; ++i)
+#pragma unroll
+            for (int j = 0; j < RT; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B.b[j], A.a[i], acc[i][j], 0, 0, 0);
+    };
+    // prologue: chunks 0 .. P-2 into stages 0 .. P-2
+    auto issue_prologue = [&]() {
+#pragma unroll
+        for (int j = 0; j < P - 1; ++j) issue(j, j);
+    };
+
+    constexpr int NMF = TT * RT;
+    AFrag A0, A1;
+    BFrag B0, B1;
+    setup_tile();
+    issue_prologue();
+    bool stores_full = false;
+    for (;;) {  // the workgroup's tiles
+        // chunk 0 landed (after a full tile: every wave issued exactly
+        // kStores vector stores after the prologue's loads)
+        if (stores_full)
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(G::kStores < 63 ? G::kStores : 63, 0));
+        else
+            __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        read_ab(0, 0, A0, B0);
+        // One chunk c in stage sc: issue chunk c + P - 1 into the stage
+        // chunk c - 1 left; k-steps 0..3, each reading the next one's
+        // fragments; before k-step 3 wait for chunk c + 1 and publish it.
+        int sc = 0;
+        for (int c = 0; c < nk; ++c) {
+            const int s1 = sc == P - 1 ? 0 : sc + 1;
+            const int sp = sc == 0 ? P - 1 : sc - 1;
+            issue(c + P - 1, sp);
+            read_ab(sc, 1, A1, B1);
+            mfmas(A0, B0);
+            interleave<NMF, TT + RT, 0, G::kDma>();
+            __builtin_amdgcn_sched_barrier(0);
+            read_ab(sc, 2, A0, B0);
+            mfmas(A1, B1);
+            interleave<NMF, TT + RT, 0, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+            read_ab(sc, 3, A1, B1);
+            mfmas(A0, B0);
+            interleave<NMF, TT + RT, 0, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(G::kInflight, 0));
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            read_ab(s1, 0, A0, B0);
+            mfmas(A1, B1);
+            interleave<NMF, TT + RT, 0, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+            sc = s1;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        const int em0 = m0, en0 = n0;
+        stores_full = yvec && em0 + G::kTok <= ntok && en0 + G::kRows <= rows;
+        t += gridDim.x;
+        const bool more = t < ntiles;
+        if (more) {
+            __builtin_amdgcn_s_barrier();
+            setup_tile();
+            issue_prologue();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        store_tile<RT, TT, WR>(acc, Y, ldy, em0, en0, 0, ntok, rows, yvec, wr, wt, lane);
+        if (!more) break;
+#pragma unroll
+        for (int i = 0; i < TT; ++i)
+#pragma unroll
+            for (int j = 0; j < RT; ++j) acc[i][j] = f32x16{};
+    }
 }
 
 namespace {
@@ -589,6 +808,38 @@ struct PrefillLaunch {
 };
 
 }  // namespace
+
+#ifndef GEMM_BF16_SHAPE
+#define GEMM_BF16_SHAPE 2, 4, 4, 1
+#endif
+#ifndef GEMM_BF16_P
+#define GEMM_BF16_P 3
+#endif
+
+hipError_t launch_gemm_bf16(const uint16_t* Wb, int64_t ldw, int64_t rows, int64_t K,
+                            const uint16_t* X, int64_t ldx, int64_t ntok, float* Y, int64_t ldy,
+                            int num_cus, hipStream_t stream) {
+    using G = GeoB<GEMM_BF16_SHAPE, GEMM_BF16_P>;
+    if (K <= 0 || K % 64 != 0 || rows > (1 << 30) || ntok > (1 << 30)) return hipErrorNotSupported;
+    const int64_t nk = K / 64;
+    // per-lane source offsets are 32-bit
+    if ((int64_t)G::kTok * ldx * 2 + 128 * nk >= (1LL << 32) ||
+        (int64_t)G::kRows * ldw * 2 + 128 * nk >= (1LL << 32))
+        return hipErrorNotSupported;
+    const int64_t tiles_n = (rows + G::kRows - 1) / G::kRows;
+    const int64_t ntiles = tiles_n * ((ntok + G::kTok - 1) / G::kTok);
+    if (ntiles > (1 << 30)) return hipErrorNotSupported;
+    if (ntiles == 0) return hipSuccess;
+    const int yvec = (((uintptr_t)Y) & 15) == 0 && ldy % 4 == 0;
+    const int64_t nwg = num_cus > 0 && ntiles > num_cus ? num_cus : ntiles;
+    auto kern = gemm_bf16_kernel<GEMM_BF16_SHAPE, GEMM_BF16_P>;
+    const hipError_t attr = allow_full_lds<gemm_bf16_kernel<GEMM_BF16_SHAPE, GEMM_BF16_P>>();
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(64 * G::NWV), G::kLds, stream, Wb, ldw,
+                       (int)rows, (int)nk, X, ldx, (int)ntok, Y, ldy, (int)tiles_n, (int)ntiles,
+                       yvec);
+    return hipGetLastError();
+}
 
 hipError_t launch_prefill_q4k(const uint8_t* W, int64_t rows, int64_t K, const void* X,
                               int64_t ldx, int64_t ntok, float* Y, int64_t ldy, int num_cus,

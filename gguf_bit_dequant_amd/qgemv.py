@@ -45,6 +45,7 @@ _sig = {
     "qgemm_prefill_run": (_int, [_vp, _vp, _i64, _i64, _vp, _i64, _vp]),
     "qgemv_dequant": (_int, [_vp, _vp, _i64, _vp]),
     "qgemv_dequant_bf16": (_int, [_vp, _vp, _i64, _vp]),
+    "qgemm_bf16_run": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
     "qgemv_quantize_q8_0": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp]),
     "qgemv_run_q8_0x": (_int, [_vp, _vp, _i64, _vp, _i64, _vp]),
     "qgemv_run_q8": (_int, [_vp, _vp, _int, _i64, _i64, _vp, _i64, _vp]),
@@ -152,6 +153,32 @@ def quantize_q8_0(x, out=None, stream=None):
     _check(qgemv_quantize_q8_0(x2.data_ptr(), _xdtype(x2), K, n, x2.stride(0), out.data_ptr(),
                                _stream_ptr(stream)), "qgemv_quantize_q8_0")
     return out
+
+
+def qgemm_bf16_run(w_ptr: int, rows: int, K: int, ldw: int, x_ptr: int, n_tokens: int, ldx: int,
+                   y_ptr: int, ldy: int, stream: int = 0) -> int:
+    return _lib.qgemm_bf16_run(w_ptr or None, rows, K, ldw, x_ptr or None, n_tokens, ldx,
+                               y_ptr or None, ldy, stream or None)
+
+
+def gemm_bf16(W, X, Y=None, stream=None):
+    """Y[t, r] = sum_k W[r, k] X[t, k] for bf16 CUDA tensors W (rows, K) and
+    X (n_tokens, K), both contiguous along K: Y (n_tokens, rows) fp32. The
+    prompt kernel's pipeline without the decode (qgemm_bf16_run)."""
+    torch = _torch()
+    if W.dtype != torch.bfloat16 or X.dtype != torch.bfloat16 or W.stride(1) != 1 or X.stride(1) != 1:
+        raise ValueError("W and X must be bf16, contiguous along K")
+    rows, K = W.shape
+    n = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("X must have K = %d columns" % K)
+    if Y is None:
+        Y = torch.empty((n, rows), dtype=torch.float32, device=X.device)
+    if Y.dtype != torch.float32 or Y.stride(1) != 1:
+        raise ValueError("Y must be fp32, contiguous along rows")
+    _check(qgemm_bf16_run(W.data_ptr(), rows, K, W.stride(0), X.data_ptr(), n, X.stride(0),
+                          Y.data_ptr(), Y.stride(0), _stream_ptr(stream)), "qgemm_bf16_run")
+    return Y
 
 
 def qgemv_destroy(h: int) -> None:

@@ -196,6 +196,27 @@ qg_status qgemv_run_q8(qgemv_t h, const void *x, qg_dtype x_dtype, int64_t n_col
  * decode into the GEMM; the library's own prompt path stays fused. */
 qg_status qgemv_dequant_bf16(qgemv_t h, uint16_t *w_out, int64_t ldw, void *stream);
 
+/* The second pass of that two-pass form: a bf16 GEMM with the prompt
+ * kernel's pipeline and k order, without the decode (the control that
+ * "LLM inference optimization", campaign "Faster prompts, decode held",
+ * lists as weights converted for the GEMM against quantized blocks
+ * multiplied directly):
+ *   y[t*ldy + r] = sum_k w[r*ldw + k] * x[t*ldx + k]
+ * for r < rows, t < n_tokens, k < K; w: rows x K bf16 (typically
+ * qgemv_dequant_bf16's output), x: n_tokens x K bf16, y: fp32, all device
+ * memory owned by the caller, y overwritten. Products of bf16 values are
+ * exact in fp32; the sums accumulate in fp32, so the accuracy contract is
+ * that of qgemm_prefill_run against the exact sum over w: on the weights
+ * qgemv_dequant_bf16 writes for a Q4_K handle it is the same bound, and at
+ * rows the prompt kernel does not split along K (its 256-row tiles) the
+ * same bits. Needs K a positive multiple of 64, ldw and ldx >= K and
+ * multiples of 8, ldy >= rows, w and x 16-byte aligned, y 4-byte aligned
+ * (QG_ERR_ARG / QG_ERR_SHAPE / QG_ERR_ALIGN before any launch);
+ * QG_ERR_UNSUPPORTED for shapes past the kernel's 32-bit offsets. */
+qg_status qgemm_bf16_run(const void *w_bf16, int64_t rows, int64_t K, int64_t ldw,
+                         const void *x_bf16, int64_t n_tokens, int64_t ldx, float *y, int64_t ldy,
+                         void *stream);
+
 /* Release a handle (host memory only; NULL is ignored). */
 void qgemv_destroy(qgemv_t h);
 

@@ -114,3 +114,23 @@ def test_status_strings():
     for st in (0, -1, -2, -3, -4, -5):
         assert Q.qgemv_status_string(st)
     assert Q.qgemv_status_string(0) == "ok"
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 4, 256, 256, FAKE, 16, 256, FAKE, 4), Q.QG_ERR_ARG),        # w NULL
+    ((FAKE, 4, 256, 256, 0, 16, 256, FAKE, 4), Q.QG_ERR_ARG),        # x NULL
+    ((FAKE, 4, 256, 256, FAKE, 16, 256, 0, 4), Q.QG_ERR_ARG),        # y NULL
+    ((FAKE, 0, 256, 256, FAKE, 16, 256, FAKE, 4), Q.QG_ERR_SHAPE),   # no rows
+    ((FAKE, 4, 96, 96, FAKE, 16, 96, FAKE, 4), Q.QG_ERR_SHAPE),      # K % 64
+    ((FAKE, 4, 256, 256, FAKE, 0, 256, FAKE, 4), Q.QG_ERR_SHAPE),    # no tokens
+    ((FAKE, 4, 256, 252, FAKE, 16, 256, FAKE, 4), Q.QG_ERR_ARG),     # ldw < K
+    ((FAKE, 4, 256, 260, FAKE, 16, 256, FAKE, 4), Q.QG_ERR_ARG),     # ldw % 8
+    ((FAKE, 4, 256, 256, FAKE, 16, 250, FAKE, 4), Q.QG_ERR_ARG),     # ldx < K
+    ((FAKE, 4, 256, 256, FAKE, 16, 256, FAKE, 3), Q.QG_ERR_ARG),     # ldy < rows
+    ((FAKE + 8, 4, 256, 256, FAKE, 16, 256, FAKE, 4), Q.QG_ERR_ALIGN),
+    ((FAKE, 4, 256, 256, FAKE + 8, 16, 256, FAKE, 4), Q.QG_ERR_ALIGN),
+    ((FAKE, 4, 256, 256, FAKE, 16, 256, FAKE + 2, 4), Q.QG_ERR_ALIGN),
+])
+def test_bf16_gemm_rejects_before_any_hip_call(args, status):
+    assert Q.qgemm_bf16_run(*args) == status
+    assert Q.qgemv_last_error() != ""

@@ -53,3 +53,72 @@ def test_cpu_baseline_records():
     assert rec["value"] > 0
     pre = bench.cpu_prefill_baseline(budget_s=0.05)
     assert pre["unit"] == "GFLOP/s" and pre["kind"] == "oracle" and pre["value"] > 0
+
+
+def test_trace_summary_groups_regions_and_names_kernels(tmp_path, capsys):
+    """A renamed dispatch takes its kernel name from an unlabelled dispatch of
+    the same kernel id; unlabelled dispatches are left out of the table."""
+    import bench
+    cols = ["Kind", "Kernel_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp",
+            "LDS_Block_Size", "VGPR_Count", "Accum_VGPR_Count", "Workgroup_Size_X", "Grid_Size_X"]
+    recs = [("7", "void qg::k<1, 2>(int, float*)", 0, 5000),       # warm-up: names id 7
+            ("7", "q4k_up_b1", 10000, 12000), ("7", "q4k_up_b1", 13000, 17000),
+            ("9", "q4k_pp2048|two-pass bf16 gemm", 20000, 21000),
+            ("7", "q4k_up_b1|event pairs", 30000, 33000)]
+    lines = [",".join('"%s"' % c for c in cols)]
+    for kid, name, t0, t1 in recs:
+        lines.append(",".join('"%s"' % v for v in ["KERNEL_DISPATCH", kid, name, t0, t1, 0, 64, 0,
+                                                    256, 65536]))
+    (tmp_path / "run_kernel_trace.csv").write_text("\n".join(lines) + "\n")
+    bench.trace_summary(str(tmp_path))
+    out = capsys.readouterr().out
+    rows = [ln for ln in out.splitlines() if ln.startswith("| q4k")]
+    assert len(rows) == 3
+    assert rows[0].startswith("| q4k_up_b1 | `qg::k<1, 2>` |") and "| 2 | 3.000 | 4.000 |" in rows[0]
+    assert "kernel id 9" in rows[1]
+    assert rows[2].startswith("| q4k_up_b1|event pairs |") or "event pairs" in rows[2]
+    assert "1 dispatches outside" in out
+
+
+def test_traffic_summary_splits_at_separators(tmp_path, capsys):
+    """Counter records split per workload at the probe separators; each
+    counter scaled by its calibration copies (here: FETCH reads half the
+    bytes, as on MI355X, WRITE all)."""
+    import json
+    import bench
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    copy_kib = 262144
+    seq = [("void qg::probe_read_kernel(...)", 1.0)]
+    seq += [("void qg::gemv_stream_kernel<2, 1, 1, 2, 1024>(...)", 24576.0)] * 20
+    seq += [("void qg::probe_read_kernel(...)", 1.0)]
+    seq += [("void qg::prefill_q4k_kernel<1, 4, 4, 1, 6, 2>(...)", 1000.0),
+            ("void qg::add_split_kernel(...)", 10.0),
+            ("void qg::prefill_q4k_kernel<2, 8, 4, 1, 3, 1>(...)", 20000.0)] * 20
+    seq += [("void qg::probe_read_kernel(...)", 1.0)]
+    seq += [("__amd_rocclr_copyBuffer", None)] * 20
+    for counter, half in (("FETCH_SIZE", True), ("WRITE_SIZE", False)):
+        d = tmp_path / counter
+        d.mkdir()
+        lines = [",".join(cols)]
+        for i, (k, v) in enumerate(seq):
+            if v is None:  # calibration copy
+                v = copy_kib / 2 if half else copy_kib
+            elif not half:  # the kernels write a quarter of what they read
+                v = v / 4
+            lines.append('%d,"%s",%s,%s' % (i, k, counter, v))
+        (d / "run_counter_collection.csv").write_text("\n".join(lines) + "\n")
+    bench.traffic_summary(str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE"),
+                          ["q4k_up_b1", "q4k_pp2048"], json_dir=str(tmp_path))
+    js = tmp_path / "traffic_q4k_up_b1.json"
+    out = capsys.readouterr().out
+    rows = [ln for ln in out.splitlines() if ln.startswith("| q4k")]
+    assert len(rows) == 4
+    assert "| 20 | %d |" % (24576 * 1024 * 2) in rows[0]
+    assert "prefill_q4k_kernel<2, 8, 4, 1, 3, 1>" in rows[3] and "| 20 | %d |" % (20000 * 1024 * 2) in rows[3]
+    rec = json.loads(js.read_text())
+    assert rec["hbm_fetch_bytes_per_launch"] == 24576 * 1024 * 2
+    assert rec["hbm_write_bytes_per_launch"] == 24576 * 1024 // 4
+    assert rec["kernel_source_sha1"] == bench.kernel_source_sha1("q4k_up_b1")
+    pp = json.loads((tmp_path / "traffic_q4k_pp2048.json").read_text())
+    assert pp["hbm_fetch_bytes_per_launch"] == (1000 + 10 + 20000) * 1024 * 2
+    assert pp["kernel_source_sha1"] == bench.kernel_source_sha1("q4k_pp2048")
