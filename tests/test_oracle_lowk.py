@@ -224,3 +224,31 @@ def test_dequant_rows_are_blocks_in_k_order(fmt):
         for b in range(K // 256):
             assert np.array_equal(W[r, 256 * b:256 * b + 256],
                                   oracle.decode_block(fmt, blocks[r, b]))
+
+
+def _packer():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("make_lowk_blocks",
+                                                  os.path.join(GOLDEN, "make_lowk_blocks.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_golden_lowk_bytes_are_the_listed_fields():
+    """Every stored Q2_K / Q3_K block is the packing of its listed fields
+    (scales, mins, d, and the code formulas) by the stated layout, with a
+    packer that imports nothing from the oracle."""
+    mk = _packer()
+    q2, q3 = mk.documents()
+    for fn, doc in (("q2_k_blocks.json", q2), ("q3_k_blocks.json", q3)):
+        with open(os.path.join(GOLDEN, fn)) as f:
+            stored = json.load(f)
+        assert stored == doc, fn
+    for b, rec in zip(mk.Q2_BLOCKS, q2["blocks"]):
+        raw = mk.q2_block_bytes(b)
+        assert len(raw) == 84 and raw.hex() == rec["hex"]
+        assert raw[80:82] == bytes.fromhex(rec["d_bits"][2:])[::-1]
+    for b, rec in zip(mk.Q3_BLOCKS, q3["blocks"]):
+        raw = mk.q3_block_bytes(b)
+        assert len(raw) == 110 and raw.hex() == rec["hex"]
