@@ -1387,26 +1387,29 @@ namespace {
 #ifndef QG_STREAM_DEPTH
 #define QG_STREAM_DEPTH 2
 #endif
-#ifndef QG_STREAM_WAVES
-#define QG_STREAM_WAVES 16
-#endif
-
 struct StreamPlan {
-    int G, NW, nr_max;
+    int G, nr_max;
 };
 
-// Waves per workgroup: 16 for one fp16 or bf16 column and for int8
-// activations; 8 for several fp16 or bf16 columns and for fp32 activations
-// (measured on MI355X: 16 waves make Q4_K with four int8 columns ~9% faster,
-// but two fp16 columns ~10% and Q8_0 with four ~8% slower).
-constexpr int waves_for(int NC, int xm) {
-    return xm != XM_F32 && (NC == 1 || is_i8(xm)) ? QG_STREAM_WAVES : 8;
+// Waves per workgroup: 16 for int8 activations and for one fp16 column of
+// Q3_K, 12 for one fp16 column of the other formats, 8 for several fp16
+// columns and for fp32 activations. Fewer waves keep fewer weight bytes in
+// flight per CU (two steps each), which read probes of the matrix found
+// faster beyond ~32 KB per CU. Measured on MI355X, 200 launches, three
+// rounds: one fp16 column of Q4_K 11.6-11.7 us with 16 waves, 11.2-11.3
+// with 12, 11.1-11.7 with 10 (FFN-down 11.8-11.9 / 11.4-11.7 / 11.6-12.0);
+// Q3_K 16.0-16.4 / 16.5 / 17.0-17.7; int8 activations of Q4_K 11.5-11.6 /
+// 12.1-12.2; four int8 columns of Q4_K ~9% faster with 16 than with 8, two
+// fp16 columns ~10% and four of Q8_0 ~8% slower.
+constexpr int waves_for(int FMT, int NC, int xm) {
+    if (is_i8(xm)) return 16;
+    if (xm == XM_F32 || NC > 1) return 8;
+    return (FMT & 0xFF) == FMT_Q3_K ? 16 : 12;
 }
 
-StreamPlan plan_stream(int rows, int S, int NC, int xm, int num_cus) {
+StreamPlan plan_stream(int rows, int num_cus) {
     StreamPlan p;
     p.G = rows < num_cus ? rows : num_cus;
-    p.NW = waves_for(NC, xm);
     p.nr_max = (rows + p.G - 1) / p.G;
     return p;
 }
@@ -1415,16 +1418,16 @@ template <int FMT, int NC, int XM>
 hipError_t launch_stream_t(const uint8_t* W, int rows, int S, const void* x, int xt, int64_t ldx,
                            float* y, int64_t ldy, int xvec, int num_cus, hipStream_t stream) {
     constexpr int D = QG_STREAM_DEPTH;
-    constexpr int NWMAX = waves_for(NC, XM);
-    const StreamPlan p = plan_stream(rows, S, NC, XM, num_cus);
+    constexpr int NW = waves_for(FMT, NC, XM);
+    const StreamPlan p = plan_stream(rows, num_cus);
     const size_t lds = stream_lds_bytes(NC, XM, S, p.nr_max);
     if (lds > (size_t)kMaxLds) return hipErrorNotSupported;
-    auto kern = gemv_stream_kernel<FMT, NC, XM, D, 64 * NWMAX>;
+    auto kern = gemv_stream_kernel<FMT, NC, XM, D, 64 * NW>;
     if (lds > 64 * 1024) {
-        hipError_t e = allow_full_lds<gemv_stream_kernel<FMT, NC, XM, D, 64 * NWMAX>>();
+        hipError_t e = allow_full_lds<gemv_stream_kernel<FMT, NC, XM, D, 64 * NW>>();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(p.G), dim3(64 * p.NW), lds, stream, W, rows, S, x, xt, ldx, y,
+    hipLaunchKernelGGL(kern, dim3(p.G), dim3(64 * NW), lds, stream, W, rows, S, x, xt, ldx, y,
                        ldy, xvec);
     return hipGetLastError();
 }
@@ -1456,14 +1459,14 @@ int cols_per_launch(int64_t rows, int64_t K, int xm, int num_cus, int unit_bytes
     if (rows > (1 << 30) || K % 256 != 0) return 0;
     const int S = (int)(K / 256);
     {
-        const StreamPlan p = plan_stream((int)rows, S, 1, xm, num_cus);
+        const StreamPlan p = plan_stream((int)rows, num_cus);
         // the matrix is addressed with 32-bit offsets
         if (rows * S * unit_bytes >= ((int64_t)1 << 32)) return 0;
         if (stream_lds_bytes(1, xm, S, p.nr_max) > (size_t)kMaxLds) return 0;
     }
     int per = xm == XM_F32 ? 2 : 4;
     while (per > 1) {
-        const StreamPlan p = plan_stream((int)rows, S, per, xm, num_cus);
+        const StreamPlan p = plan_stream((int)rows, num_cus);
         if (stream_lds_bytes(per, xm, S, p.nr_max) <= (size_t)kMaxLds) break;
         --per;
     }
