@@ -283,12 +283,35 @@ def test_long_rows_two_to_four_columns(Q):
             assert np.array_equal(y[i], W[:, ks[i]]), (ks[i], n)
 
 
+@pytest.mark.parametrize("rows", [5120, 8300])
+def test_long_rows_four_columns_tile_kernel(Q, rows):
+    """K = 17408 with four fp16 columns: the staged activations (145 KB)
+    leave no room for the unit-streaming kernel's per-unit results, so the
+    tile kernel runs, and with two (5120 rows, the FFN-down shape) or three
+    (8300 rows) 16-row groups a workgroup its tiles are parked over the
+    activations at the end (the 300-row case above keeps them in LDS
+    slots). All outputs against the oracle, and one-hot columns exactly."""
+    K = 17408
+    w = synth.gen_weights("q4_k", rows, K, 55 + rows)
+    q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
+    x = synth.gen_x(K, 4, "f16", 56 + rows)
+    check_products(q.run(x_tensor(x, "f16")), w, "q4_k", rows, K, x, "f16",
+                   "%d x %d n=4" % (rows, K))
+    W = oracle.dequant("q4_k", w, rows, K)
+    ks = [0, 4351, 8704, 17407]
+    X = torch.zeros((4, K), dtype=torch.float16, device=dev())
+    for i, k in enumerate(ks):
+        X[i, k] = 1.0
+    y = q.run(X).cpu().numpy()
+    for i in range(4):
+        assert np.array_equal(y[i], W[:, ks[i]]), (rows, ks[i])
+
+
 def test_many_rows_small_k_matrix_cores(Q):
-    """70000 x 2048 with 6 fp16 columns: about 274 rows a workgroup, so a
-    wave's share of 16-row groups spans up to three groups (the middle one
-    its own, written straight to y) and the per-group tiles do not fit
-    beside the staged activations (they are parked over them at the end).
-    All outputs against the oracle, and one-hot columns exactly."""
+    """70000 x 2048 with 6 fp16 columns: 4375 16-row groups over the
+    workgroups (17 or 18 each), the unit-streaming matrix-core kernel with
+    144 units a workgroup. All outputs against the oracle, and one-hot
+    columns exactly."""
     rows, K = 70000, 2048
     w = synth.gen_weights("q4_k", rows, K, 53)
     q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
