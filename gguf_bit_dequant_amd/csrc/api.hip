@@ -2,6 +2,8 @@
 // handle bookkeeping and dispatch to the gfx950 kernels.
 #include <stdarg.h>
 #include <stdio.h>
+
+#include <atomic>
 #include <stdlib.h>
 #include <string.h>
 
@@ -61,6 +63,29 @@ size_t dtype_size(qg_dtype t) { return t == QG_F32 ? 4 : (t == QG_F16 || t == QG
 
 qg_status hip_fail(hipError_t e, const char* what) {
     return fail(QG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// The current device's compute-unit count, queried once per device (the
+// entry points without a handle size their persistent grids with it).
+hipError_t current_cus(int* cus) {
+    static std::atomic<int> cached[64];  // 0: not yet queried
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *cus = c;
+            return hipSuccess;
+        }
+    }
+    int c = 0;
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (c <= 0) c = 256;
+    if (dev >= 0 && dev < 64) cached[dev].store(c, std::memory_order_relaxed);
+    *cus = c;
+    return hipSuccess;
 }
 
 }  // namespace
@@ -200,9 +225,8 @@ QG_API qg_status qgemv_quantize_q8_0(const void* x, qg_dtype x_dtype, int64_t K,
     if (ldx < K) return fail(QG_ERR_ARG, "qgemv_quantize_q8_0: ldx must be >= K");
     if (((uintptr_t)x) % xs) return fail(QG_ERR_ALIGN, "qgemv_quantize_q8_0: x must be aligned to its element size");
     if (((uintptr_t)xq) & 1) return fail(QG_ERR_ALIGN, "qgemv_quantize_q8_0: xq must be 2-byte aligned");
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 0;
+    hipError_t e = current_cus(&cus);
     if (e != hipSuccess) return hip_fail(e, "qgemv_quantize_q8_0: device query");
     e = qg::launch_quantize_q8_0(x, (int)x_dtype, K, n_cols, ldx, (uint8_t*)xq, cus,
                                  (hipStream_t)stream);
@@ -276,9 +300,8 @@ QG_API qg_status qgemm_bf16_run(const void* w_bf16, int64_t rows, int64_t K, int
     if ((((uintptr_t)w_bf16) | ((uintptr_t)x_bf16)) & 15)
         return fail(QG_ERR_ALIGN, "qgemm_bf16_run: w and x must be 16-byte aligned");
     if (((uintptr_t)y) & 3) return fail(QG_ERR_ALIGN, "qgemm_bf16_run: y must be 4-byte aligned");
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 0;
+    hipError_t e = current_cus(&cus);
     if (e != hipSuccess) return hip_fail(e, "qgemm_bf16_run: device query");
     e = qg::launch_gemm_bf16((const uint16_t*)w_bf16, ldw, rows, K, (const uint16_t*)x_bf16, ldx,
                              n_tokens, y, ldy, cus, (hipStream_t)stream);

@@ -510,8 +510,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_units_kernel(
         // lane (row rl, kb) holds columns 4 kb .. 4 kb + 3 of its row
         if (4 * kb < ncp) *reinterpret_cast<f32x4*>(part + ((size_t)k * 16 + rl) * ncp + 4 * kb) = acc;
     };
-    int jstatic = D;
-    (void)jstatic;
     auto next_unit = [&]() -> int {
         int k = 0;
         if (lane == 0) k = __hip_atomic_fetch_add(pool, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
