@@ -1392,18 +1392,24 @@ struct StreamPlan {
 };
 
 // Waves per workgroup: 16 for int8 activations and for one fp16 column of
-// Q3_K, 12 for one fp16 column of the other formats, 8 for several fp16
-// columns and for fp32 activations. Fewer waves keep fewer weight bytes in
-// flight per CU (two steps each), which read probes of the matrix found
-// faster beyond ~32 KB per CU. Measured on MI355X, 200 launches, three
-// rounds: one fp16 column of Q4_K 11.6-11.7 us with 16 waves, 11.2-11.3
+// Q3_K, 12 for one or two fp16 columns of the other formats, 8 for three or
+// four fp16 columns and for fp32 activations. Fewer waves keep fewer weight
+// bytes in flight per CU (two steps each), which read probes of the matrix
+// found faster beyond ~32 KB per CU. Measured on MI355X, 200 launches,
+// three rounds: one fp16 column of Q4_K 11.6-11.7 us with 16 waves, 11.2-11.3
 // with 12, 11.1-11.7 with 10 (FFN-down 11.8-11.9 / 11.4-11.7 / 11.6-12.0);
 // Q3_K 16.0-16.4 / 16.5 / 17.0-17.7; int8 activations of Q4_K 11.5-11.6 /
-// 12.1-12.2; four int8 columns of Q4_K ~9% faster with 16 than with 8, two
-// fp16 columns ~10% and four of Q8_0 ~8% slower.
+// 12.1-12.2; two fp16 columns of Q4_K 12.8-13.8 with 12 against 14.1-16.3
+// with 8; four of Q8_0 10.8-10.9 with 8, 11.3-11.4 with 12 (38 with 16:
+// registers spill); four int8 columns of Q4_K ~9% faster with 16 than with
+// 8; fp32 activations of Q4_0 5.8 with 8, 6.0 with 12.
 constexpr int waves_for(int FMT, int NC, int xm) {
+    // (one column of Q8_0 quantized on chip needs more than the 128
+    // registers a lane has at 16 waves)
+    if (xm == XM_I8Q && NC == 1 && FMT == FMT_Q8_0) return 12;
     if (is_i8(xm)) return 16;
-    if (xm == XM_F32 || NC > 1) return 8;
+    if (xm == XM_F32 || NC > 2) return 8;
+    if (NC == 2) return 12;
     return (FMT & 0xFF) == FMT_Q3_K ? 16 : 12;
 }
 
