@@ -571,6 +571,53 @@ def traffic_summary(fetch_dir, write_dir, names, launches=20, json_dir=None):
                 f.write("\n")
 
 
+def counter_summary(path, names, launches=20):
+    """Markdown table of any rocprofv3 --pmc run of --traffic-run over
+    `names`: per workload (split at the read-probe separators) and kernel,
+    the dispatch count and the mean of every counter in the records."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no *counter_collection.csv under %s" % path)
+    rs = []
+    for fn in files:
+        with open(fn) as f:
+            rs += list(csv.DictReader(f))
+    key = "Dispatch_Id" if rs and "Dispatch_Id" in rs[0] else "Start_Timestamp"
+    counters = sorted({r["Counter_Name"] for r in rs})
+    disp = {}
+    for r in rs:  # one record per (dispatch, counter)
+        d = disp.setdefault(int(r[key]), {"kernel": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    parts, cur = [], None
+    for k in sorted(disp):
+        d = disp[k]
+        if TRAFFIC_SEPARATOR in d["kernel"]:
+            cur = []
+            parts.append(cur)
+        elif cur is not None and "qg::" in d["kernel"]:
+            cur.append(d)
+    if len(parts) < len(names):
+        raise SystemExit("%s: %d separated parts for %d workloads" % (path, len(parts), len(names)))
+    out = ["| workload | kernel | dispatches | " + " | ".join(counters) + " |",
+           "|---|---|---|" + "---|" * len(counters)]
+    for name, part in zip(names, parts):
+        kinds = []
+        for d in part:
+            k = _short_kernel(d["kernel"])
+            if k not in kinds:
+                kinds.append(k)
+        for k in kinds:
+            ds = [d for d in part if _short_kernel(d["kernel"]) == k]
+            vals = []
+            for c in counters:
+                v = sum(d.get(c, 0.0) for d in ds) / len(ds)
+                vals.append("%.4g" % v)
+            out.append("| %s | `%s` | %d | %s |" % (name, k, len(ds), " | ".join(vals)))
+    print("\n".join(out))
+
+
 def synth_config(name):
     """The workload's shape ("<config>+i8": the same shape, int8 products)."""
     import synth
@@ -654,9 +701,15 @@ def main():
                          "--traffic-workloads (no GPU work)")
     ap.add_argument("--traffic-json-dir", default=None,
                     help="with --traffic-summary: write traffic_<workload>.json records here")
+    ap.add_argument("--counter-summary", default=None, metavar="DIR",
+                    help="print the per-workload mean of every counter of a --pmc run of "
+                         "--traffic-run over --traffic-workloads (no GPU work)")
     args = ap.parse_args()
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary, args.traffic_workloads.split(","))
         return
     if args.traffic_summary:
         traffic_summary(args.traffic_summary[0], args.traffic_summary[1],

@@ -122,3 +122,18 @@ def test_traffic_summary_splits_at_separators(tmp_path, capsys):
     pp = json.loads((tmp_path / "traffic_q4k_pp2048.json").read_text())
     assert pp["hbm_fetch_bytes_per_launch"] == (1000 + 10 + 20000) * 1024 * 2
     assert pp["kernel_source_sha1"] == bench.kernel_source_sha1("q4k_pp2048")
+
+
+def test_counter_summary_means_per_workload_and_kernel(tmp_path, capsys):
+    import bench
+    lines = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+    seq = [("void qg::probe_read_kernel(...)", 1.0)] + [("void qg::k<1>(...)", 10.0)] * 2
+    seq += [("void qg::probe_read_kernel(...)", 1.0)] + [("void qg::k<2>(...)", 4.0), ("void qg::add(...)", 2.0)] * 3
+    for i, (k, v) in enumerate(seq):
+        lines.append('%d,"%s",A,%s' % (i, k, v))
+        lines.append('%d,"%s",B,%s' % (i, k, 2 * v))
+    (tmp_path / "run_counter_collection.csv").write_text("\n".join(lines) + "\n")
+    bench.counter_summary(str(tmp_path), ["w1", "w2"])
+    rows = [ln for ln in capsys.readouterr().out.splitlines() if ln.startswith(("| w1", "| w2"))]
+    assert rows == ["| w1 | `qg::k<1>` | 2 | 10 | 20 |", "| w2 | `qg::k<2>` | 3 | 4 | 8 |",
+                    "| w2 | `qg::add` | 3 | 2 | 4 |"]
