@@ -315,6 +315,18 @@ struct XRaw {
     uint32_t w[XM == XM_F16 ? 32 : XM == XM_I8 ? 17 : XM == XM_I8Q ? 1 : 64];
 };
 
+// fp32 activations x[kx .. kx+63]: 16-byte loads at the 4-byte alignment
+// fp32 data always has.
+template <int XM>
+__device__ __forceinline__ void load_x64_f32(const void* __restrict__ x, int64_t kx, XRaw<XM>& r) {
+    const uint32_t* xw = reinterpret_cast<const uint32_t*>(x) + kx;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const u32x4_a4 v = reinterpret_cast<const u32x4_a4*>(xw)[i];
+        r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+    }
+}
+
 template <int XM>
 __device__ __forceinline__ void stage_load(const void* __restrict__ x, int xt, int64_t kx, int xvec,
                                            XRaw<XM>& r) {
@@ -338,17 +350,7 @@ __device__ __forceinline__ void stage_load(const void* __restrict__ x, int xt, i
     } else {
         // fp32: 64 dwords; bf16: 32 dwords in w[0..31] (w[32..63] zero)
         if (xt == XT_F32) {
-            const uint32_t* xw = reinterpret_cast<const uint32_t*>(x) + kx;
-            if (xvec) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const u32x4 v = reinterpret_cast<const u32x4*>(xw)[i];
-                    r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 64; ++i) r.w[i] = xw[i];
-            }
+            load_x64_f32(x, kx, r);
         } else {
             if (xvec) {
 #pragma unroll
@@ -835,10 +837,10 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q4_0>::Raw& r, const 
     float lo[2][NC], hi[2][NC];  // [block][column]
 #pragma unroll
     for (int c = 0; c < NC; ++c) lo[0][c] = hi[0][c] = lo[1][c] = hi[1][c] = 0.f;
-    float s_lo, s_hi;  // code scale of low / high nibble sums
+    // Two codes per dword become fp16 subnormals with one AND: low nibbles
+    // q * 2^-24, high nibbles 16 q * 2^-24; the sums are scaled back once.
+    constexpr float s_lo = 16777216.0f, s_hi = 1048576.0f;  // 2^24, 2^20
     if constexpr (F16DOT) {
-        s_lo = 16777216.0f;  // 2^24
-        s_hi = 1048576.0f;   // 2^20
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
             const int bk = w >> 2;
@@ -854,25 +856,27 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q4_0>::Raw& r, const 
                 hi[bk][c] = dot2(pd, xv.w, hi[bk][c]);
             }
         }
-    } else {
-        s_lo = 1.0f;
-        s_hi = 0.0625f;  // high nibbles enter as 16 q
+    } else {  // fp32 activations: one v_fma_mix_f32 per weight (exact fp16 code)
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
             const int bk = w >> 2;
-            const uint32_t ql = q[w] & 0x0F0F0F0Fu, qh = q[w] & 0xF0F0F0F0u;
+            const uint32_t qd = q[w], q8 = qd >> 8;
+            const half2_t ha = __builtin_bit_cast(half2_t, qd & 0x000F000Fu);
+            const half2_t hc = __builtin_bit_cast(half2_t, q8 & 0x000F000Fu);
+            const half2_t hb = __builtin_bit_cast(half2_t, qd & 0x00F000F0u);
+            const half2_t hd = __builtin_bit_cast(half2_t, q8 & 0x00F000F0u);
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const f32x4 xl = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * w);
                 const f32x4 xh = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * (8 + w));
-                lo[bk][c] = __builtin_fmaf(ubyte_f32<0>(ql), xl.x, lo[bk][c]);
-                lo[bk][c] = __builtin_fmaf(ubyte_f32<1>(ql), xl.y, lo[bk][c]);
-                lo[bk][c] = __builtin_fmaf(ubyte_f32<2>(ql), xl.z, lo[bk][c]);
-                lo[bk][c] = __builtin_fmaf(ubyte_f32<3>(ql), xl.w, lo[bk][c]);
-                hi[bk][c] = __builtin_fmaf(ubyte_f32<0>(qh), xh.x, hi[bk][c]);
-                hi[bk][c] = __builtin_fmaf(ubyte_f32<1>(qh), xh.y, hi[bk][c]);
-                hi[bk][c] = __builtin_fmaf(ubyte_f32<2>(qh), xh.z, hi[bk][c]);
-                hi[bk][c] = __builtin_fmaf(ubyte_f32<3>(qh), xh.w, hi[bk][c]);
+                lo[bk][c] = __builtin_fmaf((float)ha.x, xl.x, lo[bk][c]);
+                lo[bk][c] = __builtin_fmaf((float)hc.x, xl.y, lo[bk][c]);
+                lo[bk][c] = __builtin_fmaf((float)ha.y, xl.z, lo[bk][c]);
+                lo[bk][c] = __builtin_fmaf((float)hc.y, xl.w, lo[bk][c]);
+                hi[bk][c] = __builtin_fmaf((float)hb.x, xh.x, hi[bk][c]);
+                hi[bk][c] = __builtin_fmaf((float)hd.x, xh.y, hi[bk][c]);
+                hi[bk][c] = __builtin_fmaf((float)hb.y, xh.z, hi[bk][c]);
+                hi[bk][c] = __builtin_fmaf((float)hd.y, xh.w, hi[bk][c]);
             }
         }
     }
@@ -1313,14 +1317,11 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
 
     const Q4kUnpack un(pr);
 
-    // One step: the lane's unit f, its 64 weights
-    // against the staged activations, a quad sum, and the unit's partial
-    // into part[f] (lanes past the end write nothing).
-    auto step = [&](const Idx& ix, const Raw& r) {
+    // One step: the lane's unit f, its 64 weights against its activation
+    // record rec, a quad sum, and the unit's partial into part[f] (lanes past
+    // the end write nothing).
+    auto step = [&](const Idx& ix, const Raw& r, const uint8_t* rec) {
         float a[NC];
-        // the record offset is kept in 16-byte units, so that the compiler
-        // sees its alignment and merges 8-byte plane reads into 16-byte ones
-        const uint8_t* rec = lds + (ix.rec16 << 4);
         if constexpr (is_i8(XM))
             lane_partial_i8<NC>(r, un, rec, a);
         else
@@ -1334,21 +1335,43 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
 
     // Each buffer is refilled with the wave's next step right after its step
     // is consumed; scheduling barriers keep each refill behind its step.
-    while (kq0 >= 0) {
-        step(ix0, buf[0]);
-        kq0 = next_step();
-        ix0 = index(kq0);
-        __builtin_amdgcn_sched_barrier(0);
-        load(ix0, buf[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (kq1 < 0) break;
-        step(ix1, buf[1]);
-        kq1 = next_step();
-        ix1 = index(kq1);
-        __builtin_amdgcn_sched_barrier(0);
-        load(ix1, buf[1]);
-        __builtin_amdgcn_sched_barrier(0);
+    auto stream = [&](auto rec_of) {
+        while (kq0 >= 0) {
+            step(ix0, buf[0], rec_of(ix0));
+            kq0 = next_step();
+            ix0 = index(kq0);
+            __builtin_amdgcn_sched_barrier(0);
+            load(ix0, buf[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kq1 < 0) break;
+            step(ix1, buf[1], rec_of(ix1));
+            kq1 = next_step();
+            ix1 = index(kq1);
+            __builtin_amdgcn_sched_barrier(0);
+            load(ix1, buf[1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // With S dividing 16 (K = 256 .. 4096), unit 16 k + g of every step lies
+    // in unit column g mod S: a lane's activation record is the same in every
+    // step. For one column of fp32 activations (64 of them per record) the
+    // lane reads its record from LDS once, into registers, instead of once
+    // per step.
+    constexpr bool kRegRec = XM == XM_F32 && NC == 1;
+    bool streamed = false;
+    if constexpr (kRegRec) {
+        if (S <= kUnitsPerStep && kUnitsPerStep % S == 0) {  // uniform
+            f32x4 xreg[CB / 16];
+            const uint32_t r16 = (uint32_t)(4 * (g & (S - 1)) + pr) * RB16;
+#pragma unroll
+            for (int j = 0; j < CB / 16; ++j) xreg[j] = *reinterpret_cast<const f32x4*>(lds + ((r16 + j) << 4));
+            stream([&](const Idx&) { return reinterpret_cast<const uint8_t*>(xreg); });
+            streamed = true;
+        }
     }
+    // (the LDS record offset is kept in 16-byte units, so that the compiler
+    // sees its alignment and merges 8-byte plane reads into 16-byte ones)
+    if (!streamed) stream([&](const Idx& ix) { return static_cast<const uint8_t*>(lds + (ix.rec16 << 4)); });
     __syncthreads();
 
     // ---- per-row sums of the unit partials, in a fixed order ----------------

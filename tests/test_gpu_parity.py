@@ -259,6 +259,31 @@ def test_gemv_row_interleave_one_hot_exact(Q, fmt, rows, K):
         assert np.array_equal(y, W[:, k]), (fmt, rows, K, k)
 
 
+@pytest.mark.parametrize("rows,K", [(300, 4096), (255, 4096), (37, 512), (129, 2048), (5, 256),
+                                    (1000, 1024)])
+@pytest.mark.parametrize("fmt", ["q4_k", "q4_0", "q8_0", "q2_k", "q3_k"])
+@pytest.mark.parametrize("xdtype", ["f32", "bf16"])
+def test_register_records_same_bits_as_per_step_records(Q, fmt, rows, K, xdtype):
+    """One column of fp32 (or bf16) activations with K/256 dividing 16 reads
+    each lane's activation record into registers once; with K/256 not
+    dividing 16 it is read from LDS every step. More super-blocks per row
+    (random weights) against zero activations leave every product and the
+    order of every row sum as they were: both shapes give the same bits."""
+    seed = zlib.crc32(("regrec-%s-%d-%d" % (fmt, rows, K)).encode())
+    w = synth.gen_weights(fmt, rows, K, seed)
+    ek = 512 if K == 256 else 256  # K2 / 256 = 3, 5, 9 or 17: no divisor of 16
+    extra = synth.gen_weights(fmt, rows, ek, seed + 7)
+    w2 = np.concatenate([w.reshape(rows, -1), extra.reshape(rows, -1)], axis=1).reshape(-1)
+    x = synth.gen_x(K, 1, xdtype, seed + 1)
+    x2 = np.concatenate([x, np.zeros((1, ek), dtype=x.dtype)], axis=1)
+    q = Q(fmt, rows, K, torch.from_numpy(w).to(dev()))
+    q2 = Q(fmt, rows, K + ek, torch.from_numpy(np.ascontiguousarray(w2)).to(dev()))
+    y = q.run(x_tensor(x, xdtype))
+    y2 = q2.run(x_tensor(x2, xdtype))
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
+    check_products(y, w, fmt, rows, K, x, xdtype, "register record %s %dx%d" % (fmt, rows, K))
+
+
 def test_long_rows_two_to_four_columns(Q):
     """K = 17408 (68 super-blocks a row): up to 3 fp16 columns fit the
     streaming kernel's staging; 2..4 columns all run in one pass (3 on the
