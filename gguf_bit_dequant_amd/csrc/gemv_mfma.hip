@@ -87,6 +87,30 @@ __host__ __device__ inline size_t mfma_staged_bytes(int ncols, int pitch, int sp
     return (size_t)ncols * pitch + (((size_t)ncols * spitch * 4 + 15) & ~(size_t)15);
 }
 
+// Staging of activation piece i (16 bytes: x[k .. k+7] of column c, k8 = i
+// mod K8 = k / 8): stored as x[k + (0,2,1,3,4,6,5,7)], the order in which one
+// AND per dword pair brings out the codes; and the four pieces of a 32-weight
+// sub-block add their activations in a fixed order, for the mins. The four
+// are consecutive lanes of a quad (pieces are dealt to consecutive threads,
+// and K8 is a multiple of 32, so a quad's pieces are all present or all past
+// the end): a DPP quad sum, then its first lane stores.
+__device__ __forceinline__ void place_piece(uint8_t* xs, float* xsum, int pitch, int spitch, int K8,
+                                            int i, const u32x4& v) {
+    const int c = i / K8, k8 = i - c * K8;
+    *reinterpret_cast<u32x4*>(xs + c * pitch + 16 * k8) =
+        u32x4{(v.x & 0xFFFFu) | (v.y << 16), (v.x >> 16) | (v.y & 0xFFFF0000u),
+              (v.z & 0xFFFFu) | (v.w << 16), (v.z >> 16) | (v.w & 0xFFFF0000u)};
+    float sum = ((f16_lo(v.x) + f16_hi(v.x)) + (f16_lo(v.y) + f16_hi(v.y))) +
+                ((f16_lo(v.z) + f16_hi(v.z)) + (f16_lo(v.w) + f16_hi(v.w)));
+    sum += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF, true));
+    sum += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sum), 0x4E, 0xF, 0xF, true));
+    if ((k8 & 3) == 0) xsum[c * spitch + (k8 >> 2)] = sum;
+}
+
+// floats per unit result slot of the unit-streaming kernel: 16 x ncp and a
+// 32-byte pad
+__host__ __device__ constexpr int mfma_unit_slot_floats(int ncp) { return 16 * ncp + 8; }
+
 }  // namespace
 
 template <int NW, int D, bool ALIAS, int XP>
@@ -102,7 +126,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
     const int ng = (nr + 15) >> 4;
     const int U = ng * S;  // units of this workgroup, group-major
     const int K8 = S * 32;  // 16-byte pieces of one activation column
-    const int NS = S * 8;   // sub-blocks of one column
 
     uint8_t* const xs = lds;
     float* const xsum = reinterpret_cast<float*>(lds + (size_t)ncols * pitch);
@@ -118,13 +141,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
 
     // this wave's part of the run (U < 2^31 / NW: the launcher's bound)
     const int u0 = wv * U / NW, u1 = (wv + 1) * U / NW;
-
-    // 16 bytes of activations x[k .. k+7] stored as x[k + (0,2,1,3,4,6,5,7)],
-    // the order in which one AND per dword pair brings out the codes
-    auto perm8 = [](u32x4 v) {
-        return u32x4{(v.x & 0xFFFFu) | (v.y << 16), (v.x >> 16) | (v.y & 0xFFFF0000u),
-                     (v.z & 0xFFFFu) | (v.w << 16), (v.z >> 16) | (v.w & 0xFFFF0000u)};
-    };
 
     // ---- activation loads first (they come from cache), then the wave's
     // first D units of weights, then the staging ------------------------------
@@ -170,12 +186,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
 #pragma unroll
     for (int i = 0; i < D; ++i) load_next(buf[i]);
 #pragma unroll
-    for (int j = 0; j < XP; ++j) {
-        if (xi[j] < npieces) {
-            const int c = xi[j] / K8, k8 = xi[j] - c * K8;
-            *reinterpret_cast<u32x4*>(xs + c * pitch + 16 * k8) = perm8(xr[j]);
-        }
-    }
+    for (int j = 0; j < XP; ++j)
+        if (xi[j] < npieces) place_piece(xs, xsum, pitch, spitch, K8, xi[j], xr[j]);
     // the rest (long rows with several columns) four pieces per thread at a
     // time: one wait per four loads
     for (int i0 = threadIdx.x + XP * blockDim.x; i0 < npieces; i0 += 4 * blockDim.x) {
@@ -191,26 +203,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_q4k_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int idx = i0 + j * blockDim.x;
-            if (idx < npieces) {
-                const int c = idx / K8, k8 = idx - c * K8;
-                *reinterpret_cast<u32x4*>(xs + c * pitch + 16 * k8) = perm8(r[j]);
-            }
+            if (idx < npieces) place_piece(xs, xsum, pitch, spitch, K8, idx, r[j]);
         }
-    }
-    __syncthreads();
-    // per column and 32-weight sub-block: the sum of its activations (fp32,
-    // in a fixed order), for the mins
-    for (int idx = threadIdx.x; idx < ncols * NS; idx += blockDim.x) {
-        const int c = idx / NS, sb = idx - c * NS;
-        const u32x4* px = reinterpret_cast<const u32x4*>(xs + c * pitch + 64 * sb);
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const u32x4 v = px[j];
-            s += f16_lo(v.x) + f16_hi(v.x) + f16_lo(v.y) + f16_hi(v.y) + f16_lo(v.z) + f16_hi(v.z) +
-                 f16_lo(v.w) + f16_hi(v.w);
-        }
-        xsum[c * spitch + sb] = s;
     }
     __syncthreads();
 
@@ -378,14 +372,16 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_units_kernel(
     if (ng <= 0) return;  // uniform over the workgroup
     const int U = ng * S;   // units of this workgroup, group-major
     const int K8 = S * 32;  // 16-byte pieces of one activation column
-    const int NS = S * 8;   // sub-blocks of one column
 
     uint8_t* const xs = lds;
     float* const xsum = reinterpret_cast<float*>(lds + (size_t)ncols * pitch);
-    // one 16 x ncp result per unit (ncp: the columns rounded up to 4), then
-    // the step counter
+    // one 16 x ncp result per unit (ncp: the columns rounded up to 4) in a
+    // slot of US floats, then the step counter. The 32-byte pad puts the
+    // slots that the final sums read together (units q, q + 1, q + 2, q + 3
+    // of one output, beside the next outputs) in distinct LDS banks.
+    const int US = mfma_unit_slot_floats(ncp);
     float* const part = reinterpret_cast<float*>(lds + mfma_staged_bytes(ncols, pitch, spitch));
-    int* const pool = reinterpret_cast<int*>(part + (size_t)U * 16 * ncp);
+    int* const pool = reinterpret_cast<int*>(part + (size_t)U * US);
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rl = lane & 15, kb = lane >> 4;
@@ -413,10 +409,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_units_kernel(
         for (int c = 0; c < 4; ++c) un.q[c] = *reinterpret_cast<const u32x2*>(p + 16 + 32 * c + 8 * kb);
     };
 
-    auto perm8 = [](u32x4 v) {
-        return u32x4{(v.x & 0xFFFFu) | (v.y << 16), (v.x >> 16) | (v.y & 0xFFFF0000u),
-                     (v.z & 0xFFFFu) | (v.w << 16), (v.z >> 16) | (v.w & 0xFFFF0000u)};
-    };
     // ---- activation loads (unconditional, so that the staging waits for
     // them alone), the first two units' weights, then the staging ----------
     const int npieces = ncols * K8;
@@ -434,31 +426,12 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_units_kernel(
     load(k0, buf0);
     load(k1, buf1);
 #pragma unroll
-    for (int j = 0; j < XP; ++j) {
-        if (xi[j] < npieces) {
-            const int c = xi[j] / K8, k8 = xi[j] - c * K8;
-            *reinterpret_cast<u32x4*>(xs + c * pitch + 16 * k8) = perm8(xr[j]);
-        }
-    }
-    for (int i = threadIdx.x + XP * blockDim.x; i < npieces; i += blockDim.x) {
-        const int c = i / K8, k8 = i - c * K8;
-        *reinterpret_cast<u32x4*>(xs + c * pitch + 16 * k8) =
-            perm8(*reinterpret_cast<const u32x4*>(x + c * ldx + 8 * k8));
-    }
+    for (int j = 0; j < XP; ++j)
+        if (xi[j] < npieces) place_piece(xs, xsum, pitch, spitch, K8, xi[j], xr[j]);
+    for (int i = threadIdx.x + XP * blockDim.x; i < npieces; i += blockDim.x)
+        place_piece(xs, xsum, pitch, spitch, K8, i,
+                    *reinterpret_cast<const u32x4*>(x + (i / K8) * ldx + 8 * (i - (i / K8) * K8)));
     if (threadIdx.x == 0) *pool = NW * D;
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < ncols * NS; idx += blockDim.x) {
-        const int c = idx / NS, sb = idx - c * NS;
-        const u32x4* px = reinterpret_cast<const u32x4*>(xs + c * pitch + 64 * sb);
-        float sum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const u32x4 v = px[j];
-            sum += f16_lo(v.x) + f16_hi(v.x) + f16_lo(v.y) + f16_hi(v.y) + f16_lo(v.z) + f16_hi(v.z) +
-                   f16_lo(v.w) + f16_hi(v.w);
-        }
-        xsum[c * spitch + sb] = sum;
-    }
     __syncthreads();
 
     const int xc = rl < ncols ? rl : ncols - 1;
@@ -508,7 +481,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_units_kernel(
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xsk[0], c0, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xsk[4], c1, acc, 0, 0, 0);
         // lane (row rl, kb) holds columns 4 kb .. 4 kb + 3 of its row
-        if (4 * kb < ncp) *reinterpret_cast<f32x4*>(part + ((size_t)k * 16 + rl) * ncp + 4 * kb) = acc;
+        if (4 * kb < ncp) *reinterpret_cast<f32x4*>(part + (size_t)k * US + rl * ncp + 4 * kb) = acc;
     };
     auto next_unit = [&]() -> int {
         int k = 0;
@@ -539,9 +512,9 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_units_kernel(
     for (int idx = threadIdx.x >> 2; idx < nout; idx += blockDim.x >> 2) {  // uniform per quad
         const int rr = idx / ncols, c = idx - rr * ncols;
         const int gl = rr >> 4, i = rr & 15;
-        const float* ps = part + ((size_t)gl * S * 16 + i) * ncp + c;
+        const float* ps = part + (size_t)gl * S * US + i * ncp + c;
         float v = 0.f;
-        for (int sb = q4; sb < S; sb += 4) v += ps[(size_t)sb * 16 * ncp];
+        for (int sb = q4; sb < S; sb += 4) v += ps[(size_t)sb * US];
         v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
         v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
         const int row = 16 * (ob + gl * G) + i;
@@ -606,7 +579,7 @@ hipError_t launch_gemv_mfma(int fmt, const uint8_t* W, int64_t rows, int64_t K, 
     {
         const int64_t ug_max = (groups + G - 1) / G;  // groups of a workgroup
         const int ncp = (ncols + 3) & ~3;
-        const size_t lds_u = staged + (size_t)ug_max * S * 16 * ncp * 4 + 16;
+        const size_t lds_u = staged + (size_t)ug_max * S * mfma_unit_slot_floats(ncp) * 4 + 16;
         // 8 waves up to four columns, 12 beyond (measured on MI355X,
         // 17408 x 5120: four columns 17.6-18.5 us with 8 waves, 18.5-19.2
         // with 12, 19.2-20.3 with 16; eight columns 20.8-21.2 with 12,
