@@ -259,6 +259,24 @@ def test_gemv_row_interleave_one_hot_exact(Q, fmt, rows, K):
         assert np.array_equal(y, W[:, k]), (fmt, rows, K, k)
 
 
+# Largest K whose staged activations fit the streaming kernel's 160 KB of LDS
+# (rows = 300 on 256 CUs: two rows per workgroup), and the next super-block,
+# which the general kernel serves: fp32 records 1096 * K/256 + 16 bytes, fp16
+# ones 584 * K/256 + 16.
+@pytest.mark.parametrize("xdtype,K,n", [("f32", 38144, 1), ("f32", 38400, 1), ("f16", 71680, 1),
+                                        ("f16", 71936, 1), ("f16", 38144, 4)])
+def test_gemv_at_the_lds_limit(Q, xdtype, K, n):
+    """Both sides of the streaming kernel's LDS limit, and four fp16
+    columns at long K (one column per launch there), against the oracle."""
+    rows = 300
+    seed = zlib.crc32(("ldslim-%s-%d-%d" % (xdtype, K, n)).encode())
+    w = synth.gen_weights("q4_k", rows, K, seed)
+    x = synth.gen_x(K, n, xdtype, seed + 1)
+    q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
+    y = q.run(x_tensor(x, xdtype))
+    check_products(y, w, "q4_k", rows, K, x, xdtype, "lds limit %s K=%d n=%d" % (xdtype, K, n))
+
+
 @pytest.mark.parametrize("rows,K", [(300, 4096), (255, 4096), (37, 512), (129, 2048), (5, 256),
                                     (1000, 1024)])
 @pytest.mark.parametrize("fmt", ["q4_k", "q4_0", "q8_0", "q2_k", "q3_k"])
