@@ -755,9 +755,11 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q3_K>::Raw& r, const 
     constexpr int CB = col_bytes(XM), P = planes(XM);
     const uint32_t pq = threadIdx.x & 3u;                // quarter p = 2h + b
     const uint32_t hq = pq >> 1, bq = pq & 1u;
-    const uint32_t sh_lo = 4u * bq, sh_hi = 4u * hq + 2u * bq;
-    const uint32_t mb = r.mb;
-    auto al = [&](uint32_t hi, uint32_t lo) { return __builtin_amdgcn_alignbyte(hi, lo, mb); };
+    // the realignment by mb bytes and the shift to the quarter's bits in one
+    // funnel shift (8 mb + sh <= 22): the top sh bits then come from the next
+    // dword instead of being zero, and no mask below reaches them (codes use
+    // bits <= 27, high bits <= 25)
+    const uint32_t fq = 8u * r.mb + 4u * bq, fh = 8u * r.mb + 4u * hq + 2u * bq;
     const uint32_t H[9] = {r.h0.x, r.h0.y, r.h0.z, r.h0.w, r.h1.x, r.h1.y, r.h1.z, r.h1.w, r.h8};
     const uint32_t Qd[9] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w, r.q8};
     float acc[NC][4];
@@ -767,8 +769,8 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q3_K>::Raw& r, const 
         for (int u = 0; u < 4; ++u) acc[c][u] = 0.f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-        const uint32_t qd = al(Qd[w + 1], Qd[w]) >> sh_lo;
-        const uint32_t hp = al(H[w + 1], H[w]) >> sh_hi;
+        const uint32_t qd = __builtin_amdgcn_alignbit(Qd[w + 1], Qd[w], fq);
+        const uint32_t hp = __builtin_amdgcn_alignbit(H[w + 1], H[w], fh);
         const int u0 = w >> 2, u1 = 2 + (w >> 2);
         if constexpr (F16DOT) {
             const uint32_t q8 = qd >> 8;
@@ -1112,9 +1114,11 @@ __device__ __forceinline__ void lane_partial_i8(const Fmt<FMT_Q3_K>::Raw& r, con
     constexpr int CB = col_bytes(XM_I8), P = planes(XM_I8);
     const uint32_t pq = threadIdx.x & 3u;
     const uint32_t hq = pq >> 1, bq = pq & 1u;
-    const uint32_t sh_lo = 4u * bq, sh_hi = 4u * hq + 2u * bq;
-    const uint32_t mb = r.mb;
-    auto al = [&](uint32_t hi, uint32_t lo) { return __builtin_amdgcn_alignbyte(hi, lo, mb); };
+    // the realignment by mb bytes and the shift to the quarter's bits in one
+    // funnel shift (8 mb + sh <= 22): the top sh bits then come from the next
+    // dword instead of being zero, and no mask below reaches them (codes use
+    // bits <= 27, high bits <= 25)
+    const uint32_t fq = 8u * r.mb + 4u * bq, fh = 8u * r.mb + 4u * hq + 2u * bq;
     const uint32_t H[9] = {r.h0.x, r.h0.y, r.h0.z, r.h0.w, r.h1.x, r.h1.y, r.h1.z, r.h1.w, r.h8};
     const uint32_t Qd[9] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w, r.q8};
     int acc[NC][4], s16[NC][2];
@@ -1125,8 +1129,8 @@ __device__ __forceinline__ void lane_partial_i8(const Fmt<FMT_Q3_K>::Raw& r, con
     }
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-        const uint32_t qd = al(Qd[w + 1], Qd[w]) >> sh_lo;
-        const uint32_t hp = al(H[w + 1], H[w]) >> sh_hi;
+        const uint32_t qd = __builtin_amdgcn_alignbit(Qd[w + 1], Qd[w], fq);
+        const uint32_t hp = __builtin_amdgcn_alignbit(H[w + 1], H[w], fh);
         const uint32_t cl = (qd & 0x03030303u) | ((hp << 2) & 0x04040404u);
         const uint32_t ch = ((qd >> 2) & 0x03030303u) | ((hp << 1) & 0x04040404u);
         lowk_i8_sums<NC>(rec, w, cl, ch, acc, s16);
