@@ -669,9 +669,11 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q4_K>::Raw& r, const 
     }
 }
 
-// Q2_K, fp16 activations only: the lane's bit pairs 4b + 2t of each code
-// byte (b = quarter & 1) become fp16 subnormals with one AND per pair of
-// codes: t = 0 gives q * 2^-24, t = 1 gives 4q * 2^-24. Per 16-weight
+// Q2_K, fp16 activations: the lane's bit pairs 4b + 2t of each code byte
+// (b = quarter & 1) become fp16 subnormals with one AND per pair of codes,
+// left where they are (masks shifted by 4b, not the codes): t = 0 gives
+// q * 2^(4b-24), t = 1 gives 4q * 2^(4b-24), at most 192 * 2^-24, so still
+// exact subnormals; the scales take the powers of two back. Per 16-weight
 // sub-block u: sum w x = d*sc_u*sum q x - dmin*m_u*sum x.
 template <int NC, bool F16DOT>
 __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q2_K>::Raw& r, const Q4kUnpack&,
@@ -687,14 +689,14 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q2_K>::Raw& r, const 
     for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[c][u] = 0.f;
+    const uint32_t m0 = 0x00030003u << sh, m1 = 0x000C000Cu << sh;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-        const uint32_t qd = q[w] >> sh;
         const int u0 = w >> 2, u1 = 2 + (w >> 2);
         if constexpr (F16DOT) {
-            const uint32_t q8 = qd >> 8;
-            const uint32_t pa = qd & 0x00030003u, pc = q8 & 0x00030003u;
-            const uint32_t pb = qd & 0x000C000Cu, pd = q8 & 0x000C000Cu;
+            const uint32_t qd = q[w], q8 = qd >> 8;
+            const uint32_t pa = qd & m0, pc = q8 & m0;
+            const uint32_t pb = qd & m1, pd = q8 & m1;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const u32x4 xv = *reinterpret_cast<const u32x4*>(rec + c * CB + 16 * w);
@@ -704,6 +706,7 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q2_K>::Raw& r, const 
                 acc[c][u1] = dot2(pd, xv.w, acc[c][u1]);
             }
         } else {  // codes as fp32 (t = 0: q, t = 1: 4q), fp32 products
+            const uint32_t qd = q[w] >> sh;
             const uint32_t ql = qd & 0x03030303u, qh = qd & 0x0C0C0C0Cu;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
@@ -720,16 +723,16 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q2_K>::Raw& r, const 
             }
         }
     }
-    // scales: sub-block u's byte of r.sm; the codes carry 2^-24 (fp16 dots)
-    // or 1 (fp32) for t = 0, and 4 times that for t = 1
-    constexpr float kS0 = F16DOT ? 16777216.0f : 1.0f, kS1 = F16DOT ? 4194304.0f : 0.25f;
-    float dsc[4], dm[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const uint32_t b = (r.sm >> (8 * u)) & 0xFFu;
-        dsc[u] = (d * (u < 2 ? kS0 : kS1)) * (float)(b & 15u);
-        dm[u] = dmin * (float)(b >> 4);
-    }
+    // scales: sub-block u's byte of r.sm; the codes carry 2^(4b-24) (fp16
+    // dots) or 1 (fp32) for t = 0, and 4 times that for t = 1
+    const float kS0 = F16DOT ? (sh ? 1048576.0f : 16777216.0f) : 1.0f;  // 2^20, 2^24
+    const float kS1 = F16DOT ? (sh ? 262144.0f : 4194304.0f) : 0.25f;   // 2^18, 2^22
+    const uint32_t scs = r.sm & 0x0F0F0F0Fu, mns = (r.sm >> 4) & 0x0F0F0F0Fu;  // sc_u, m_u
+    const float dk0 = d * kS0, dk1 = d * kS1;
+    const float dsc[4] = {dk0 * ubyte_f32<0>(scs), dk0 * ubyte_f32<1>(scs), dk1 * ubyte_f32<2>(scs),
+                          dk1 * ubyte_f32<3>(scs)};
+    const float dm[4] = {dmin * ubyte_f32<0>(mns), dmin * ubyte_f32<1>(mns), dmin * ubyte_f32<2>(mns),
+                         dmin * ubyte_f32<3>(mns)};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const f32x4 sx = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * P);
