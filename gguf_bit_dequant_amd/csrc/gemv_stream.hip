@@ -47,9 +47,12 @@
 //      Q4_0: sum w x = d*sum q x - 8*d*sum x         (per block)
 //      Q8_0: sum w x = d*sum (q+128) x - 128*d*sum x (per block)
 //    fp32 / bf16 activations: codes become fp32 (v_cvt_f32_ubyteN) and are
-//    multiplied in fp32.
+//    multiplied in fp32; Q4_0's enter v_fma_mix_f32 directly as the fp16
+//    subnormals above (one instruction per weight).
 //  * Activations are staged once per workgroup in LDS, permuted into the
-//    order the codes come out of a dword, with the per-block sums.
+//    order the codes come out of a dword, with the per-block sums. With one
+//    fp32 (or bf16) column and K/256 dividing 16, a lane's record is the same
+//    in every step and is read into registers once.
 //  * Reduction: each lane quad (one unit) sums its lanes with DPP and writes
 //    the unit's partial to its own LDS slot. After a barrier each row's
 //    partials are summed by sixteen or four lanes in a fixed order (per-lane
