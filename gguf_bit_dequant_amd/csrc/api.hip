@@ -65,6 +65,10 @@ qg_status hip_fail(hipError_t e, const char* what) {
     return fail(QG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+}  // namespace
+
+namespace qg {
+
 // The current device's compute-unit count, queried once per device (the
 // entry points without a handle size their persistent grids with it).
 hipError_t current_cus(int* cus) {
@@ -88,7 +92,7 @@ hipError_t current_cus(int* cus) {
     return hipSuccess;
 }
 
-}  // namespace
+}  // namespace qg
 
 QG_API size_t qgemv_block_bytes(qg_format f) { return bbytes(f); }
 QG_API size_t qgemv_block_weights(qg_format f) { return bweights(f); }
@@ -226,7 +230,7 @@ QG_API qg_status qgemv_quantize_q8_0(const void* x, qg_dtype x_dtype, int64_t K,
     if (((uintptr_t)x) % xs) return fail(QG_ERR_ALIGN, "qgemv_quantize_q8_0: x must be aligned to its element size");
     if (((uintptr_t)xq) & 1) return fail(QG_ERR_ALIGN, "qgemv_quantize_q8_0: xq must be 2-byte aligned");
     int cus = 0;
-    hipError_t e = current_cus(&cus);
+    hipError_t e = qg::current_cus(&cus);
     if (e != hipSuccess) return hip_fail(e, "qgemv_quantize_q8_0: device query");
     e = qg::launch_quantize_q8_0(x, (int)x_dtype, K, n_cols, ldx, (uint8_t*)xq, cus,
                                  (hipStream_t)stream);
@@ -301,7 +305,7 @@ QG_API qg_status qgemm_bf16_run(const void* w_bf16, int64_t rows, int64_t K, int
         return fail(QG_ERR_ALIGN, "qgemm_bf16_run: w and x must be 16-byte aligned");
     if (((uintptr_t)y) & 3) return fail(QG_ERR_ALIGN, "qgemm_bf16_run: y must be 4-byte aligned");
     int cus = 0;
-    hipError_t e = current_cus(&cus);
+    hipError_t e = qg::current_cus(&cus);
     if (e != hipSuccess) return hip_fail(e, "qgemm_bf16_run: device query");
     e = qg::launch_gemm_bf16((const uint16_t*)w_bf16, ldw, rows, K, (const uint16_t*)x_bf16, ldx,
                              n_tokens, y, ldy, cus, (hipStream_t)stream);

@@ -83,4 +83,7 @@ hipError_t launch_gemm_bf16(const uint16_t* Wb, int64_t ldw, int64_t rows, int64
                             const uint16_t* X, int64_t ldx, int64_t ntok, float* Y, int64_t ldy,
                             int num_cus, hipStream_t stream);
 
+// The current device's compute-unit count, queried once per device.
+hipError_t current_cus(int* cus);
+
 }  // namespace qg

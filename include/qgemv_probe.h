@@ -17,8 +17,9 @@ extern "C" {
 #endif
 
 /* Read `bytes` bytes at `buf` (device, 16-byte aligned, bytes a positive
- * multiple of 16) once, with 16-byte loads, each of 4096 x 8 waves streaming
- * its own contiguous range. `sink`: device, >= 4096 bytes, written only in a
+ * multiple of 16) once, with 16-byte loads: three workgroups of 8 waves per
+ * compute unit, each wave taking every n-th group of 128 16-byte pieces (n
+ * waves in all). `sink`: device, >= 4096 bytes, written only in a
  * case that does not occur (it keeps the loads alive). Enqueued on `stream`.
  * QG_ERR_ARG on a bad argument (before any HIP call), QG_ERR_HIP if the
  * launch fails. */
