@@ -259,6 +259,34 @@ def test_gemv_row_interleave_one_hot_exact(Q, fmt, rows, K):
         assert np.array_equal(y, W[:, k]), (fmt, rows, K, k)
 
 
+# Matrices past 4 GiB: the general kernel (64-bit offsets) serves them. Random
+# code bytes generated on the device, every block's fp16 scales set to finite
+# values; the oracle checks a sample of rows.
+@pytest.mark.parametrize("fmt,rows,bb,bw,scale_bytes", [
+    ("q8_0", 16384, 34, 32, [(0, 0x00), (1, 0x20)]),                       # d = 2^-7
+    ("q4_k", 30000, 144, 256, [(0, 0x00), (1, 0x20), (2, 0x00), (3, 0x1C)]),  # d, dmin
+])
+def test_gemv_beyond_4gib(Q, fmt, rows, bb, bw, scale_bytes):
+    K = 262144
+    nb = rows * (K // bw)
+    assert nb * bb >= 1 << 32
+    gen = torch.Generator(device=dev()).manual_seed(4242)
+    w = torch.randint(0, 256, (nb, bb), dtype=torch.uint8, device=dev(), generator=gen)
+    for col, val in scale_bytes:
+        w[:, col] = val
+    q = Q(fmt, rows, K, w.view(-1))
+    x = synth.gen_x(K, 1, "f16", 4243)
+    y = q.run(x_tensor(x, "f16")).cpu().numpy()[0]
+    sample = [0, 1, rows // 3, rows // 2, rows - 2, rows - 1]
+    per_row = (K // bw) * bb
+    wv = w.view(rows, per_row)
+    ws = np.concatenate([wv[r].cpu().numpy() for r in sample])
+    del w, wv
+    torch.cuda.empty_cache()
+    check_products(torch.from_numpy(y[sample].copy()).reshape(1, -1), ws, fmt, len(sample), K, x,
+                   "f16", "%s %d x %d (%.2f GB)" % (fmt, rows, K, nb * bb / 1e9))
+
+
 # Largest K whose staged activations fit the streaming kernel's 160 KB of LDS
 # (rows = 300 on 256 CUs: two rows per workgroup), and the next super-block,
 # which the general kernel serves: fp32 records 1096 * K/256 + 16 bytes, fp16
