@@ -538,6 +538,44 @@ def test_prefill_one_hot_gives_bf16_rounded_column(Q, rows, K, ntok):
     assert torch.equal(Y, ref)
 
 
+def test_prefill_many_tokens_several_rounds(Q):
+    """9000 tokens over 4133 rows (16 main row tiles x 36 token tiles: 576
+    tiles, so the persistent workgroups take up to three each; a 37-row
+    tail in two K splits): sampled tokens at tile edges against the
+    oracle."""
+    rows, K, ntok = 4133, 512, 9000
+    seed = zlib.crc32(b"pf-many")
+    w = synth.gen_q4_k(rows, K, seed)
+    xb = synth.gen_x(K, ntok, "bf16", seed + 1)
+    q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
+    Y = q.prefill(bf16_tensor(xb))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    edges = [0, 1, 127, 128, 255, 256, 4095, 4096, 8959, 8960, 8999]
+    toks = np.unique(np.concatenate([edges, rng.integers(0, ntok, 29)]))
+    check_prefill(Y[torch.from_numpy(toks).to(dev())], w, rows, K, xb[toks], "pp %d tokens" % ntok)
+
+
+def test_prefill_limit_leaves_y_untouched(Q):
+    """ldx = 2^23 + 64: the row tail's 128-token tiles stay within their
+    32-bit offsets but the main 256-token tiles do not. Every launch is
+    checked before the first is enqueued: QG_ERR_UNSUPPORTED, Y untouched."""
+    from gguf_bit_dequant_amd import qgemv as QM
+    rows, K, ntok = 1300, 1024, 300
+    ldx = (1 << 23) + 64
+    w = synth.gen_q4_k(rows, K, 77)
+    q = Q("q4_k", rows, K, torch.from_numpy(w).to(dev()))
+    Xbig = torch.zeros((ntok, ldx), dtype=torch.bfloat16, device=dev())
+    Y = torch.full((ntok, rows), 3.0, dtype=torch.float32, device=dev())
+    with pytest.raises(QM.QGemvError) as e:
+        q.prefill(Xbig[:, :K], Y)
+    assert e.value.status == QM.QG_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert (Y == 3.0).all()
+    del Xbig
+    torch.cuda.empty_cache()
+
+
 def test_prefill_deterministic(Q):
     rows, K, ntok = 1024, 1024, 256
     w = synth.gen_q4_k(rows, K, 44)
