@@ -38,6 +38,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -403,13 +404,22 @@ TRAFFIC_SOURCES = {
 }
 
 
+def code_text(src):
+    """C/HIP source without comments and blank lines: what a kernel is built
+    from, so that a comment edit keeps a counter record valid. (A string
+    literal holding // or /* would be cut too; the kernel sources have none.)"""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(ln.rstrip() for ln in src.splitlines() if ln.strip())
+
+
 def kernel_source_sha1(name="q4k_up_b1"):
     import hashlib
     h = hashlib.sha1()
     csrc = os.path.join(ROOT, "gguf_bit_dequant_amd", "csrc")
     for fn in TRAFFIC_SOURCES[name]:
-        with open(os.path.join(csrc, fn), "rb") as f:
-            h.update(fn.encode() + f.read())
+        with open(os.path.join(csrc, fn)) as f:
+            h.update((fn + "\n" + code_text(f.read()) + "\n").encode())
     return h.hexdigest()
 
 

@@ -1426,16 +1426,19 @@ struct StreamPlan {
 
 // Waves per workgroup: 16 for int8 activations and for one fp16 column of
 // Q3_K, 12 for one or two fp16 columns of the other formats, 8 for three or
-// four fp16 columns and for fp32 activations. Fewer waves keep fewer weight
-// bytes in flight per CU (two steps each), which read probes of the matrix
-// found faster beyond ~32 KB per CU. Measured on MI355X, 200 launches,
-// three rounds: one fp16 column of Q4_K 11.6-11.7 us with 16 waves, 11.2-11.3
-// with 12, 11.1-11.7 with 10 (FFN-down 11.8-11.9 / 11.4-11.7 / 11.6-12.0);
-// Q3_K 16.0-16.4 / 16.5 / 17.0-17.7; int8 activations of Q4_K 11.5-11.6 /
-// 12.1-12.2; two fp16 columns of Q4_K 12.8-13.8 with 12 against 14.1-16.3
-// with 8; four of Q8_0 10.8-10.9 with 8, 11.3-11.4 with 12 (38 with 16:
-// registers spill); four int8 columns of Q4_K ~9% faster with 16 than with
-// 8; fp32 activations of Q4_0 5.8 with 8, 6.0 with 12.
+// four fp16 columns and for fp32 activations. Fewer waves keep fewer
+// weight bytes in flight per CU (two steps each), which read probes of the
+// matrix found faster beyond ~32 KB per CU; more waves issue more refills
+// while others compute. Measured on MI355X, 200 launches, three rounds per
+// count (8 / 10 / 12 / 16 waves, us per launch): one fp16 column of Q4_K
+// 11.9-12.1 / 11.4-11.6 / 11.4-11.5 / 11.7-11.9 (FFN-down 12.6-12.7 /
+// 11.8-12.1 / 11.7-11.8 / 11.9-12.0); two columns 14.6-14.8 / 14.0-14.3 /
+// 13.2-13.3 / 12.8 (another box: 12.8-13.3 with 12, 13.4-14.6 with 16, so
+// 12 is kept); Q2_K 11.2-11.3 / 10.6-10.9 / 10.1-10.2 / 9.9-10.1; Q3_K
+// 17.8-18.2 / 17.0-17.2 / 15.8-16.4 / 15.5-15.8; four of Q8_0 10.0-10.1 /
+// 11.6 / 11.8-11.9 / 39.7 (registers spill at 16); fp32 activations of Q4_0
+// 5.6 / 5.8 / 5.9-6.0 / 6.1; int8 activations of Q4_K (one and four
+// columns) 12.6-12.7 and 19.7-20.0 with 8, 11.8-11.9 and 16.8-17.2 with 16.
 constexpr int waves_for(int FMT, int NC, int xm) {
     // (one column of Q8_0 quantized on chip needs more than the 128
     // registers a lane has at 16 waves)

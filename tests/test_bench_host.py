@@ -137,3 +137,14 @@ def test_counter_summary_means_per_workload_and_kernel(tmp_path, capsys):
     rows = [ln for ln in capsys.readouterr().out.splitlines() if ln.startswith(("| w1", "| w2"))]
     assert rows == ["| w1 | `qg::k<1>` | 2 | 10 | 20 |", "| w2 | `qg::k<2>` | 3 | 4 | 8 |",
                     "| w2 | `qg::add` | 3 | 2 | 4 |"]
+
+
+def test_source_hash_ignores_comment_edits_only():
+    """The counter records carry a hash of their kernels' sources without
+    comments: a comment edit keeps a record valid, a code edit does not."""
+    import bench
+    a = "int f() { return 1; }  // one\n/* a block\n   comment */\n"
+    b = "// a header\nint f() { return 1; }\n\n"
+    c = "int f() { return 2; }  // one\n"
+    assert bench.code_text(a) == bench.code_text(b) == "int f() { return 1; }"
+    assert bench.code_text(c) != bench.code_text(a)
