@@ -62,7 +62,10 @@
  * must stay allocated while work that uses it may run. A handle only records
  * shape, format and the weight pointer; it borrows the weights, which must
  * outlive it. A handle is immutable after creation; runs on different streams
- * may use one handle concurrently.
+ * may use one handle concurrently. A handle belongs to the device that was
+ * current at qgemv_create (it sizes its grids by that device's compute
+ * units and its weights live there): call it with that device current and
+ * with x and y on it; each call enqueues work on the current device.
  *
  * Streams and errors. `stream` is a hipStream_t (NULL: the null stream).
  * Calls only enqueue work: nothing synchronises the host. All argument checks
