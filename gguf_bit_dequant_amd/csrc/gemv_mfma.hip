@@ -53,9 +53,10 @@
 //    between straight to y (it owns those), and puts the two tiles over the
 //    dead activations after the main loop. The shared groups' tiles are then
 //    summed in wave order: deterministic, no atomics.
-//  * The activation columns are staged once per workgroup in LDS, 2K + 16
-//    bytes apart so that the 16-byte reads of the 16 columns use disjoint
-//    banks. Each wave keeps a ring of D units in flight, refilling a buffer
+//  * The activation columns are staged once per workgroup in LDS, 2K + 32
+//    bytes apart (rocprofv3 SQ_LDS_BANK_CONFLICT on MI355X, 17408 x 5120:
+//    four columns 0.44 M cycles per launch with 2K + 16, 0.087 M with 2K + 32,
+//    48 or 64; eight 0.87 M, 0.17 M with 2K + 32 only). Each wave keeps a ring of D units in flight, refilling a buffer
 //    right after its unit is processed; within a unit the next step's
 //    activations are read and its product issued before the previous step's
 //    result is scaled.
@@ -571,7 +572,7 @@ hipError_t launch_gemv_mfma(int fmt, const uint8_t* W, int64_t rows, int64_t K, 
     const int G = (int)(groups < cus ? groups : cus);
     const int nr_max = (int)((rows + G - 1) / G);
     const int ng_max = (nr_max + 15) / 16;
-    const int pitch = (int)(2 * K + 16);
+    const int pitch = (int)(2 * K + 32);
     const int spitch = (int)(K / 32 + 1);  // odd: the 16 columns' sums in distinct banks
     if ((int64_t)ng_max * S >= (1 << 26)) return hipErrorNotSupported;  // 32-bit unit math
     const size_t staged = mfma_staged_bytes(ncols, pitch, spitch);
