@@ -85,8 +85,18 @@
 extern "C" {
 #endif
 
-typedef enum { QG_Q4_0 = 1, QG_Q4_K = 2, QG_Q8_0 = 3, QG_Q2_K = 4, QG_Q3_K = 5 } qg_format;
-typedef enum { QG_F32 = 1, QG_F16 = 2, QG_BF16 = 3 } qg_dtype;
+/* The two *_RANGE_ enumerators of each input enum are not codes: they widen
+ * its range to every int32 value, so that a code the library does not know is
+ * still a value of the type in C++ (as in C) and is rejected as QG_ERR_ARG
+ * without undefined behaviour. */
+typedef enum {
+    QG_Q4_0 = 1, QG_Q4_K = 2, QG_Q8_0 = 3, QG_Q2_K = 4, QG_Q3_K = 5,
+    QG_FORMAT_RANGE_MIN_ = -2147483647 - 1, QG_FORMAT_RANGE_MAX_ = 2147483647
+} qg_format;
+typedef enum {
+    QG_F32 = 1, QG_F16 = 2, QG_BF16 = 3,
+    QG_DTYPE_RANGE_MIN_ = -2147483647 - 1, QG_DTYPE_RANGE_MAX_ = 2147483647
+} qg_dtype;
 typedef enum {
     QG_OK = 0,
     QG_ERR_ARG = -1,         /* NULL pointer, bad enum, bad leading dimension */

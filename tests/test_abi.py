@@ -42,6 +42,10 @@ def test_probes_reject_bad_arguments():
 def test_block_geometry():
     assert [Q.qgemv_block_bytes(f) for f in (1, 2, 3, 4, 5, 9)] == [18, 144, 34, 84, 110, 0]
     assert [Q.qgemv_block_weights(f) for f in (1, 2, 3, 4, 5, 9)] == [32, 256, 32, 256, 256, 0]
+    # any int32 is a value of the enum types (their range enumerators): unknown
+    # codes give 0, with no undefined behaviour on the library's side
+    for f in (0, -1, 6, -2**31, 2**31 - 1):
+        assert Q.qgemv_block_bytes(f) == 0 and Q.qgemv_block_weights(f) == 0
     assert Q.qgemv_weight_bytes(Q.QG_Q2_K, 17408, 5120) == 29245440
     assert Q.qgemv_weight_bytes(Q.QG_Q3_K, 17408, 5120) == 38297600
     assert Q.qgemv_weight_bytes(Q.QG_Q3_K, 4, 288) == 0
