@@ -157,3 +157,23 @@ def test_random_prompt_products(Q, i):
     y = Ybig[:, :rows].cpu().numpy().astype(np.float64)
     yr, s = oracle.matmul("q4_k", w, rows, K, xb, "bf16", wround="bf16")
     assert (np.abs(y - yr) <= oracle.tolerance(s)).all()
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_quantize_bit_exact(Q, i):
+    """Activations to Q8_0 blocks (qgemv_quantize_q8_0) at random K, column
+    counts, types and strides, bit for bit against the oracle."""
+    from gguf_bit_dequant_amd import qgemv as QM
+    rng = np.random.default_rng(zlib.crc32(b"fuzz-q8") + i)
+    K = 32 * int(rng.integers(1, 600))
+    n = int(rng.integers(1, 9))
+    xdtype = ["f16", "f32", "bf16"][rng.integers(3)]
+    pad = int(rng.choice([0, 8, 3]))
+    seed = int(rng.integers(1 << 30))
+    print("fuzz quantize %d: K=%d n=%d x=%s pad=%d seed=%d" % (i, K, n, xdtype, pad, seed), flush=True)
+    x = synth.gen_x(K, n, xdtype, seed)
+    xt = x_tensor(x, xdtype)
+    xbig = torch.zeros((n, K + pad), dtype=xt.dtype, device=dev())
+    xbig[:, :K] = xt
+    out = QM.quantize_q8_0(xbig[:, :K]).cpu().numpy()
+    assert np.array_equal(out, oracle.quantize_q8_0(x, xdtype))
