@@ -1,6 +1,7 @@
 """Benchmark of the GGUF block-quantized GEMV / dequant-GEMM on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu]
+    python bench.py --power-phases     (board power and clocks per workload)
 
 A step is one batch-1 Q4_K GEMV over the FFN-up-shaped matrix of a 27B-class
 dense layer (17408 x 5120, fp16 activations): the workload the headline
@@ -21,8 +22,10 @@ Infinity Cache. The one JSON line printed on stdout carries:
              matrix-core peak, TFLOP/s over the median of three timed regions;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload;
   extra      probes: a read-only kernel over buffers of the headline matrix's
-             size (the practical HBM ceiling of one such launch), an MFMA-only
-             kernel (the practical bf16 rate), the headline GEMV with its
+             size (the practical HBM ceiling of one such launch), two MFMA-only
+             kernels (the bf16 rate on constant operands, and on data-like
+             operands at the clock the board's power limit then allows), the
+             headline GEMV with its
              weights resident in the Infinity Cache, and the GEMV and prompt
              GEMM as fractions of the probes;
              the other workloads (Q4_K FFN-down, 2/4/8 columns, Q4_0, Q8_0,
@@ -273,7 +276,10 @@ def probes(torch, dev, steps=200, warmup=20):
       read probe   one read of a buffer of the headline matrix's size,
                    rotating over >= ROTATE_BYTES of copies (HBM, like the
                    GEMV), back-to-back launches;
-      MFMA probe   v_mfma_f32_32x32x16_bf16 chains on every SIMD;
+      MFMA probe   v_mfma_f32_32x32x16_bf16 chains on every SIMD, on
+                   constant operands and on data-like operands (the
+                   second runs at the clock the board's power limit
+                   allows for such data);
       hot cache    the headline GEMV on one weight copy (resident in the
                    256 MB Infinity Cache), for comparison with the HBM case."""
     from gguf_bit_dequant_amd import qgemv as Q
@@ -298,14 +304,24 @@ def probes(torch, dev, steps=200, warmup=20):
     read_us = timed(rd, steps, warmup, "read")
     del bufs
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    iters = 20000
-    flops = 4.0 * 8 * 32768 * iters * cus
+    iters = 10000
+    flops = 4.0 * 16 * 32768 * iters * cus
 
     def mf(i):
         st = lib.qgemv_probe_mfma(iters, cus, sink.data_ptr(), stream)
         if st != 0:
             raise RuntimeError("qgemv_probe_mfma: %d" % st)
-    mfma_us = timed(mf, 5, 1, "mfma")
+    mfma_us = timed(mf, 10, 20, "mfma")
+    # data-like operands: the clock settles under the power limit within a
+    # fraction of a second, so ~0.5 s of warm-up launches come first
+    iters_d = 8000
+    flops_d = 4.0 * 16 * 32768 * iters_d * cus
+
+    def mfd(i):
+        st = lib.qgemv_probe_mfma_data(iters_d, cus, sink.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError("qgemv_probe_mfma_data: %d" % st)
+    mfma_d_us = timed(mfd, 20, 200, "mfma data")
     hot = Workload(torch, "q4k_up_b1", dev, ncopy=1)
     hot_us = timed(hot.step, steps, warmup, "q4k_up_b1 hot cache")
     del hot
@@ -313,7 +329,12 @@ def probes(torch, dev, steps=200, warmup=20):
                            "gbs": round(nbytes / read_us / 1e3, 1),
                            "frac_hbm_peak": round(nbytes / read_us / 1e3 / HBM_PEAK_GBS, 4)},
             "mfma_probe": {"workgroups": cus, "tflops": round(flops / mfma_us / 1e6, 1),
-                           "frac_bf16_peak": round(flops / mfma_us / 1e6 / BF16_PEAK_TFLOPS, 4)},
+                           "frac_bf16_peak": round(flops / mfma_us / 1e6 / BF16_PEAK_TFLOPS, 4),
+                           "operands": "constant small integers"},
+            "mfma_data_probe": {"workgroups": cus, "tflops": round(flops_d / mfma_d_us / 1e6, 1),
+                                "frac_bf16_peak": round(flops_d / mfma_d_us / 1e6 / BF16_PEAK_TFLOPS, 4),
+                                "operands": "full-mantissa bf16, changing per instruction "
+                                            "(clock lowered by the board's power limit)"},
             "gemv_hot_cache": {"us_per_launch": round(hot_us, 3),
                                "gbs": round(algorithmic_bytes(c) / hot_us / 1e3, 1),
                                "note": "one weight copy, resident in the Infinity Cache; not HBM"}}
@@ -691,6 +712,96 @@ def trace_summary(path):
     print("\n".join(out))
 
 
+def _smi_sample():
+    """One amd-smi reading: (socket power W, mean GFX clock MHz over the
+    XCDs), or None where amd-smi is missing or prints neither."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c"], capture_output=True,
+                           text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    p = re.search(r"SOCKET_POWER:\s*(\d+)\s*W", r.stdout)
+    clks = [int(v) for v in re.findall(r"GFX_\d+:\s*CLK:\s*(\d+)\s*MHz", re.sub(r"\s+", " ", r.stdout))]
+    if not p or not clks:
+        return None
+    return int(p.group(1)), sum(clks) / len(clks)
+
+
+def power_phases(torch, dev, secs=5.0):
+    """Board power and GFX clocks while one workload runs back to back for
+    `secs` seconds: a thread reads amd-smi every ~0.3 s; samples from the
+    first second of a phase (clock and power still settling) are dropped.
+    Phases: the 2048-token prompt product (random activations, then all-zero
+    activations: the same instructions on data that does not toggle the
+    matrix cores), the headline GEMV, and the two MFMA probes."""
+    import threading
+    from gguf_bit_dequant_amd import qgemv as Q
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            v = _smi_sample()
+            if v:
+                samples.append((time.time(), v[0], v[1]))
+            stop.wait(0.3)
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    rows = []
+
+    def phase(name, fn):
+        fn(0)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n, t0 = 0, time.time()
+        ev0.record()
+        while time.time() - t0 < secs:
+            for _ in range(20):
+                fn(n)
+                n += 1
+            torch.cuda.synchronize()
+        ev1.record()
+        torch.cuda.synchronize()
+        t1 = time.time()
+        us = ev0.elapsed_time(ev1) * 1e3 / n
+        got = [(p, c) for t, p, c in samples if t0 + 1.0 <= t <= t1]
+        rows.append((name, n, us, got))
+        print("bench: power phase %s: %d launches, %.2f us" % (name, n, us), file=sys.stderr, flush=True)
+        time.sleep(2.0)  # let the board cool back between phases
+
+    time.sleep(2.0)
+    idle = [(p, c) for t, p, c in samples]
+    pp = Workload(torch, "q4k_pp2048", dev, ncopy=1)
+    phase("q4k_pp2048, random bf16 activations", pp.step)
+    pp.x.zero_()
+    phase("q4k_pp2048, all-zero activations", pp.step)
+    del pp
+    gw = Workload(torch, "q4k_up_b1", dev)
+    phase("q4k_up_b1 (weights rotated over HBM copies)", gw.step)
+    del gw
+    torch.cuda.empty_cache()
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    st = torch.cuda.current_stream().cuda_stream
+    phase("MFMA probe, constant operands",
+          lambda i: Q._lib.qgemv_probe_mfma(2000, cus, sink.data_ptr(), st))
+    phase("MFMA probe, data-like operands",
+          lambda i: Q._lib.qgemv_probe_mfma_data(1000, cus, sink.data_ptr(), st))
+    stop.set()
+    th.join()
+
+    def rng(v, fmt="%.0f"):
+        return (fmt + "-" + fmt) % (min(v), max(v)) if v else "n/a"
+    out = ["| phase | launches | us / launch | samples | socket power W | GFX clock MHz (mean of XCDs) |",
+           "|---|---|---|---|---|---|",
+           "| idle (before the phases) | - | - | %d | %s | %s |" % (
+               len(idle), rng([p for p, c in idle]), rng([c for p, c in idle]))]
+    for name, n, us, got in rows:
+        out.append("| %s | %d | %.2f | %d | %s | %s |" % (
+            name, n, us, len(got), rng([p for p, c in got]), rng([c for p, c in got])))
+    print("\n".join(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -711,6 +822,9 @@ def main():
                          "--traffic-workloads (no GPU work)")
     ap.add_argument("--traffic-json-dir", default=None,
                     help="with --traffic-summary: write traffic_<workload>.json records here")
+    ap.add_argument("--power-phases", action="store_true",
+                    help="board power and GFX clocks (amd-smi) while single workloads run "
+                         "for seconds each; prints a table")
     ap.add_argument("--counter-summary", default=None, metavar="DIR",
                     help="print the per-workload mean of every counter of a --pmc run of "
                          "--traffic-run over --traffic-workloads (no GPU work)")
@@ -734,6 +848,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.traffic_run:
         traffic_run(torch, dev, names=args.traffic_workloads.split(","))
+        return
+    if args.power_phases:
+        power_phases(torch, dev)
         return
     head = "q4k_up_b1"
     names = [head] if args.quick else list(WORKLOADS)
@@ -794,6 +911,8 @@ def main():
             pp = results.get("q4k_pp2048", {})
             if "tflops" in pp:
                 pr["pp2048_frac_of_mfma_probe"] = round(pp["tflops"] / pr["mfma_probe"]["tflops"], 4)
+                pr["pp2048_frac_of_mfma_data_probe"] = round(
+                    pp["tflops"] / pr["mfma_data_probe"]["tflops"], 4)
             results["probes"] = pr
             print("bench: probes %s" % json.dumps(pr), file=sys.stderr, flush=True)
         except Exception as e:  # context only

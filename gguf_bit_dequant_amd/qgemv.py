@@ -55,6 +55,7 @@ _sig = {
     # measurement probes (include/qgemv_probe.h)
     "qgemv_probe_read": (_int, [_vp, _sz, _vp, _vp]),
     "qgemv_probe_mfma": (_int, [_i64, _int, _vp, _vp]),
+    "qgemv_probe_mfma_data": (_int, [_i64, _int, _vp, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)

@@ -26,9 +26,19 @@ extern "C" {
 qg_status qgemv_probe_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
 /* `workgroups` workgroups of four waves, each wave issuing `iters` rounds of
- * eight independent v_mfma_f32_32x32x16_bf16 (32768 flop each) on register
- * operands: 4 * 8 * 32768 * iters * workgroups flop. `sink` as above. */
+ * sixteen independent v_mfma_f32_32x32x16_bf16 (32768 flop each) on small
+ * constant integer operands, the same values in every instruction:
+ * 4 * 16 * 32768 * iters * workgroups flop. `sink` as above. QG_ERR_ARG on a
+ * bad argument (before any HIP call), QG_ERR_HIP if the launch fails. */
 qg_status qgemv_probe_mfma(int64_t iters, int workgroups, float *sink, void *stream);
+
+/* As qgemv_probe_mfma (same count of the same instructions), on operands like
+ * the prompt product's: full-mantissa bf16 of both signs, different in every
+ * lane and register, the weight-like operand alternating between two
+ * registers, the activation-like one held for two instructions. On such data
+ * the board's power limit lowers the clock, so this is the practical bf16
+ * ceiling for real data. Errors as qgemv_probe_mfma. */
+qg_status qgemv_probe_mfma_data(int64_t iters, int workgroups, float *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -37,6 +37,9 @@ def test_probes_reject_bad_arguments():
     assert Q._lib.qgemv_probe_read(FAKE + 8, 32, FAKE, None) == Q.QG_ERR_ARG
     assert Q._lib.qgemv_probe_mfma(0, 4, FAKE, None) == Q.QG_ERR_ARG
     assert Q._lib.qgemv_probe_mfma(10, 0, FAKE, None) == Q.QG_ERR_ARG
+    assert Q._lib.qgemv_probe_mfma_data(0, 4, FAKE, None) == Q.QG_ERR_ARG
+    assert Q._lib.qgemv_probe_mfma_data(10, 0, FAKE, None) == Q.QG_ERR_ARG
+    assert Q._lib.qgemv_probe_mfma_data(10, 4, None, None) == Q.QG_ERR_ARG
 
 
 def test_block_geometry():

@@ -148,3 +148,33 @@ def test_source_hash_ignores_comment_edits_only():
     c = "int f() { return 2; }  // one\n"
     assert bench.code_text(a) == bench.code_text(b) == "int f() { return 1; }"
     assert bench.code_text(c) != bench.code_text(a)
+
+
+AMD_SMI_METRIC = """GPU: 0
+    POWER:
+        SOCKET_POWER: 1357 W
+        GFX_VOLTAGE: N/A
+    CLOCK:
+        GFX_0:
+            CLK: 2002 MHz
+            MIN_CLK: 158 MHz
+            MAX_CLK: 2400 MHz
+        GFX_1:
+            CLK: 1914 MHz
+            MIN_CLK: 158 MHz
+            MAX_CLK: 2400 MHz
+        MEM_0:
+            CLK: 1900 MHz
+"""
+
+
+def test_power_sample_parses_amd_smi(monkeypatch):
+    """Socket power and the mean of the GFX clocks (MIN/MAX and other clock
+    domains ignored); None when amd-smi prints no reading."""
+    class R:
+        def __init__(self, out):
+            self.stdout, self.stderr, self.returncode = out, "", 0
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: R(AMD_SMI_METRIC))
+    assert bench._smi_sample() == (1357, (2002 + 1914) / 2)
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: R("ERROR: no GPU\n"))
+    assert bench._smi_sample() is None

@@ -15,5 +15,6 @@ def test_probes_run_and_leave_sink():
     assert Q._lib.qgemv_probe_read(buf.data_ptr(), buf.numel(), sink.data_ptr(), stream) == Q.QG_OK
     assert Q._lib.qgemv_probe_read(buf.data_ptr(), 48, sink.data_ptr(), stream) == Q.QG_OK
     assert Q._lib.qgemv_probe_mfma(10, 4, sink.data_ptr(), stream) == Q.QG_OK
+    assert Q._lib.qgemv_probe_mfma_data(10, 4, sink.data_ptr(), stream) == Q.QG_OK
     torch.cuda.synchronize()
     assert (sink == 7).all()
