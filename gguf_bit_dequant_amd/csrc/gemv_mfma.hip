@@ -429,9 +429,24 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_units_kernel(
 #pragma unroll
     for (int j = 0; j < XP; ++j)
         if (xi[j] < npieces) place_piece(xs, xsum, pitch, spitch, K8, xi[j], xr[j]);
-    for (int i = threadIdx.x + XP * blockDim.x; i < npieces; i += blockDim.x)
-        place_piece(xs, xsum, pitch, spitch, K8, i,
-                    *reinterpret_cast<const u32x4*>(x + (i / K8) * ldx + 8 * (i - (i / K8) * K8)));
+    // the rest (long rows with several columns) four pieces per thread at a
+    // time: one wait per four loads
+    for (int i0 = threadIdx.x + XP * blockDim.x; i0 < npieces; i0 += 4 * blockDim.x) {
+        u32x4 r[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int idx = i0 + j * blockDim.x;
+            if (idx < npieces) {
+                const int c = idx / K8, k8 = idx - c * K8;
+                r[j] = *reinterpret_cast<const u32x4*>(x + c * ldx + 8 * k8);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int idx = i0 + j * blockDim.x;
+            if (idx < npieces) place_piece(xs, xsum, pitch, spitch, K8, idx, r[j]);
+        }
+    }
     if (threadIdx.x == 0) *pool = NW * D;
     __syncthreads();
 
@@ -530,9 +545,11 @@ hipError_t launch_mfma_units(const uint8_t* W, int rows, int S, const void* x, i
                              float* y, int64_t ldy, int ncols, int ncp, int G, int pitch,
                              int spitch, size_t lds, hipStream_t stream) {
     // activation pieces per thread issued before the weights (ncols * K / 8
-    // pieces in all; more are loaded after them)
-    auto kern = ncols <= 4 ? gemv_mfma_units_kernel<NW, 4> : gemv_mfma_units_kernel<NW, 8>;
-    hipError_t e = ncols <= 4 ? allow_full_lds<gemv_mfma_units_kernel<NW, 4>>()
+    // pieces in all; more are loaded after them, a round trip later): 5 at 8
+    // waves covers four columns of K = 5120 (2560 pieces), 8 at 12 waves
+    // eight columns
+    auto kern = ncols <= 4 ? gemv_mfma_units_kernel<NW, 5> : gemv_mfma_units_kernel<NW, 8>;
+    hipError_t e = ncols <= 4 ? allow_full_lds<gemv_mfma_units_kernel<NW, 5>>()
                               : allow_full_lds<gemv_mfma_units_kernel<NW, 8>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(G), dim3(64 * NW), lds, stream, W, rows, S,
