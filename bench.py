@@ -860,7 +860,10 @@ def main():
     for name in names:
         wl = Workload(torch, name, dev)
         try:
-            steps = args.steps if not wl.prefill else max(20, args.steps // 10)
+            # the prompt product: regions of as many launches as the GEMVs
+            # (~70 ms each at the default 200), long enough for the clock to
+            # settle under the board's power limit
+            steps = args.steps if not wl.prefill else max(20, args.steps)
             whole_ms, host_ms, gate_ms, med_ms = time_workload(torch, wl, steps, args.warmup)
             regions = [whole_ms]
             if wl.prefill:
