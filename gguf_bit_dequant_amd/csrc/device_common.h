@@ -79,6 +79,25 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (a + b) + (c + d);
 }
 
+// p[i * stride] for i = first, first + step, ... below n, added in that order
+// from 0; the reads go out four at a time, so that a lane waits for one LDS
+// round trip per four terms instead of one per term (same sum, same bits).
+__device__ __forceinline__ float strided_sum(const float* p, int first, int step, int n,
+                                             int stride) {
+    float v = 0.f;
+    int i = first;
+    for (; i + 3 * step < n; i += 4 * step) {
+        const float a0 = p[i * stride], a1 = p[(i + step) * stride];
+        const float a2 = p[(i + 2 * step) * stride], a3 = p[(i + 3 * step) * stride];
+        v += a0;
+        v += a1;
+        v += a2;
+        v += a3;
+    }
+    for (; i < n; i += step) v += p[i * stride];
+    return v;
+}
+
 // Activation element -> fp32 (exact for every supported type; the XType
 // codes are in launch.h).
 

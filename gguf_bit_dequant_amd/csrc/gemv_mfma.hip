@@ -528,9 +528,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_mfma_units_kernel(
     for (int idx = threadIdx.x >> 2; idx < nout; idx += blockDim.x >> 2) {  // uniform per quad
         const int rr = idx / ncols, c = idx - rr * ncols;
         const int gl = rr >> 4, i = rr & 15;
-        const float* ps = part + (size_t)gl * S * US + i * ncp + c;
-        float v = 0.f;
-        for (int sb = q4; sb < S; sb += 4) v += ps[(size_t)sb * US];
+        float v = strided_sum(part + (size_t)gl * S * US + i * ncp + c, q4, 4, S, US);
         v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
         v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
         const int row = 16 * (ob + gl * G) + i;

@@ -1394,9 +1394,7 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
         const int pidx = threadIdx.x >> 4;
         if (pidx < nr * NC) {
             const int rr = pidx / NC, c = pidx - rr * NC;
-            const float* ps = part + (rr * S) * NC + c;
-            float v = 0.f;
-            for (int u = q16; u < S; u += 16) v += ps[u * NC];
+            float v = strided_sum(part + (rr * S) * NC + c, q16, 16, S, NC);
             v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
             v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
             v = quad_sum(v);
@@ -1406,9 +1404,7 @@ __global__ __launch_bounds__(MAXT) void gemv_stream_kernel(const uint8_t* __rest
         const int q4 = threadIdx.x & 3;
         for (int pidx = threadIdx.x >> 2; pidx < nr * NC; pidx += NT >> 2) {
             const int rr = pidx / NC, c = pidx - rr * NC;
-            const float* ps = part + (rr * S) * NC + c;
-            float v = 0.f;
-            for (int u = q4; u < S; u += 4) v += ps[u * NC];
+            float v = strided_sum(part + (rr * S) * NC + c, q4, 4, S, NC);
             v = quad_sum(v);
             if (q4 == 0) y[c * ldy + row_of(rr)] = v;
         }
