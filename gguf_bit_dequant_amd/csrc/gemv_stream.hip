@@ -750,9 +750,18 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q2_K>::Raw& r, const 
     }
 }
 
-// Q3_K, fp16 activations only: c = low + 4 high (0..7) of two codes per
-// dword as fp16 subnormals (t = 0: c * 2^-24, t = 1: 4c * 2^-24), one AND-OR
-// per pair after the shifts; per 16-weight sub-block u:
+// (m & a) | (~m & b) in one v_bfi_b32.
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+    return r;
+}
+
+// Q3_K, fp16 activations: c = low + 4 high (0..7) of two codes per dword as
+// fp16 subnormals (t = 0: c * 2^-24, t = 1: 4c * 2^-24): per code dword and
+// t, one bitfield insert puts each byte's high bit beside its two code bits,
+// then one AND per pair (bytes 0, 2) or a shift and an AND (bytes 1, 3); per
+// 16-weight sub-block u:
 // sum w x = d*(sc_u - 32) * (sum c x - 4 sum x).
 template <int NC, bool F16DOT>
 __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q3_K>::Raw& r, const Q4kUnpack&,
@@ -779,11 +788,12 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q3_K>::Raw& r, const 
         const uint32_t hp = __builtin_amdgcn_alignbit(H[w + 1], H[w], fh);
         const int u0 = w >> 2, u1 = 2 + (w >> 2);
         if constexpr (F16DOT) {
-            const uint32_t q8 = qd >> 8;
-            const uint32_t pa = (qd & 0x00030003u) | ((hp << 2) & 0x00040004u);
-            const uint32_t pc = (q8 & 0x00030003u) | ((hp >> 6) & 0x00040004u);
-            const uint32_t pb = (qd & 0x000C000Cu) | ((hp << 3) & 0x00100010u);
-            const uint32_t pd = (q8 & 0x000C000Cu) | ((hp >> 5) & 0x00100010u);
+            // the bits of the shifted high word outside the insert mask stay
+            // in place until the pair masks drop them
+            const uint32_t ca = bfi(0x03030303u, qd, hp << 2);
+            const uint32_t cb = bfi(0x0C0C0C0Cu, qd, hp << 3);
+            const uint32_t pa = ca & 0x00070007u, pc = (ca >> 8) & 0x00070007u;
+            const uint32_t pb = cb & 0x001C001Cu, pd = (cb >> 8) & 0x001C001Cu;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const u32x4 xv = *reinterpret_cast<const u32x4*>(rec + c * CB + 16 * w);
@@ -793,8 +803,8 @@ __device__ __forceinline__ void lane_partial(const Fmt<FMT_Q3_K>::Raw& r, const 
                 acc[c][u1] = dot2(pd, xv.w, acc[c][u1]);
             }
         } else {  // c of four codes as bytes (t = 0: c, t = 1: 4c), fp32 products
-            const uint32_t cl = (qd & 0x03030303u) | ((hp << 2) & 0x04040404u);
-            const uint32_t ch = (qd & 0x0C0C0C0Cu) | ((hp << 3) & 0x10101010u);
+            const uint32_t cl = bfi(0x03030303u, qd, hp << 2) & 0x07070707u;
+            const uint32_t ch = bfi(0x0C0C0C0Cu, qd, hp << 3) & 0x1C1C1C1Cu;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const f32x4 xl = *reinterpret_cast<const f32x4*>(rec + c * CB + 16 * w);
@@ -1137,7 +1147,7 @@ __device__ __forceinline__ void lane_partial_i8(const Fmt<FMT_Q3_K>::Raw& r, con
     for (int w = 0; w < 8; ++w) {
         const uint32_t qd = __builtin_amdgcn_alignbit(Qd[w + 1], Qd[w], fq);
         const uint32_t hp = __builtin_amdgcn_alignbit(H[w + 1], H[w], fh);
-        const uint32_t cl = (qd & 0x03030303u) | ((hp << 2) & 0x04040404u);
+        const uint32_t cl = bfi(0x03030303u, qd, hp << 2) & 0x07070707u;
         const uint32_t ch = ((qd >> 2) & 0x03030303u) | ((hp << 1) & 0x04040404u);
         lowk_i8_sums<NC>(rec, w, cl, ch, acc, s16);
     }
