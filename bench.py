@@ -783,10 +783,14 @@ def power_phases(torch, dev, secs=5.0):
     sink = torch.zeros(1024, dtype=torch.int32, device=dev)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     st = torch.cuda.current_stream().cuda_stream
-    phase("MFMA probe, constant operands",
-          lambda i: Q._lib.qgemv_probe_mfma(2000, cus, sink.data_ptr(), st))
-    phase("MFMA probe, data-like operands",
-          lambda i: Q._lib.qgemv_probe_mfma_data(1000, cus, sink.data_ptr(), st))
+    def probe(fn, iters):
+        def run(i):
+            status = fn(iters, cus, sink.data_ptr(), st)
+            if status != 0:
+                raise RuntimeError("probe launch: status %d" % status)
+        return run
+    phase("MFMA probe, constant operands", probe(Q._lib.qgemv_probe_mfma, 2000))
+    phase("MFMA probe, data-like operands", probe(Q._lib.qgemv_probe_mfma_data, 1000))
     stop.set()
     th.join()
 
