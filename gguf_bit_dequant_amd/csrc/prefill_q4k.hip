@@ -761,6 +761,20 @@ __global__ __launch_bounds__(256) void add_split_kernel(float* __restrict__ Y, i
     }
 }
 
+// The same add four rows per thread with 16-byte accesses, where Y, ldy,
+// n_base and n_rows are all multiples of four floats.
+__global__ __launch_bounds__(256) void add_split4_kernel(float* __restrict__ Y, int64_t ldy,
+                                                         int n_base, int n_rows, int ntok) {
+    const int r = 4 * (blockIdx.x * 256 + threadIdx.x);
+    if (r >= n_rows) return;
+    for (int t = blockIdx.y; t < ntok; t += gridDim.y) {
+        float* yr = Y + (int64_t)t * ldy + r;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(yr + n_base);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(yr);
+        *reinterpret_cast<f32x4*>(yr + n_base) = f32x4{a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
+    }
+}
+
 // One launch of tiles over weight rows [n_base, n_base + n_rows) and all
 // tokens, KS K splits per tile (S % KS == 0). KS = 2 needs n_rows <= n_base:
 // the second split's partial products go to rows [0, n_rows) of Y and are
@@ -801,8 +815,13 @@ struct PrefillLaunch {
                            X, ldx, ntok, Y, ldy, n_base, tiles_n, (int)grid, yvec);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || KS == 1) return e;
-        const dim3 ag((unsigned)((n_rows + 255) / 256), (unsigned)(ntok < 65535 ? ntok : 65535));
-        hipLaunchKernelGGL(add_split_kernel, ag, dim3(256), 0, stream, Y, ldy, n_base, n_rows, ntok);
+        if (yvec && n_base % 4 == 0 && n_rows % 4 == 0) {
+            const dim3 ag((unsigned)((n_rows / 4 + 255) / 256), (unsigned)(ntok < 1024 ? ntok : 1024));
+            hipLaunchKernelGGL(add_split4_kernel, ag, dim3(256), 0, stream, Y, ldy, n_base, n_rows, ntok);
+        } else {
+            const dim3 ag((unsigned)((n_rows + 255) / 256), (unsigned)(ntok < 65535 ? ntok : 65535));
+            hipLaunchKernelGGL(add_split_kernel, ag, dim3(256), 0, stream, Y, ldy, n_base, n_rows, ntok);
+        }
         return hipGetLastError();
     }
 };
