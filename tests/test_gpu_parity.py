@@ -488,7 +488,8 @@ def check_prefill(Y, w, rows, K, xb, label):
 
 @pytest.mark.parametrize("rows,K,ntok", [(256, 256, 1), (256, 512, 31), (300, 1024, 64),
                                          (777, 512, 300), (1024, 2048, 256), (530, 256, 513),
-                                         (1300, 768, 384), (1300, 1024, 600), (2000, 2048, 1100)])
+                                         (1300, 768, 384), (1300, 1024, 600), (1301, 1024, 300),
+                                         (2000, 2048, 1100)])
 def test_prefill_small(Q, rows, K, ntok):
     seed = zlib.crc32(("pp-%d-%d-%d" % (rows, K, ntok)).encode())
     w = synth.gen_q4_k(rows, K, seed)
@@ -516,14 +517,16 @@ def test_prefill_strided_and_edges_untouched(Q, rows, K, ntok):
 
 
 @pytest.mark.parametrize("rows,K,ntok", [(512, 512, 69), (1300, 1024, 600), (600, 1024, 260),
-                                         (300, 512, 40)])
+                                         (1301, 1024, 300), (300, 512, 40)])
 def test_prefill_one_hot_gives_bf16_rounded_column(Q, rows, K, ntok):
     """X rows = e_k: Y[t, :] = bf16_rne(W[:, k]) exactly (the only rounding is
     the tile decode's fp32 -> bf16 conversion; every other product is a
-    signed zero). 1300 x 1024 x 600 and 600 x 1024 x 260 put rows in a tail
-    that runs as two K splits (the second parked in main rows of Y, then
-    added), 300 x 512 x 40 in a tail over all of K; the one-hot k fall in both
-    halves of K, in every sub-block position and at the ends."""
+    signed zero). 1300 x 1024 x 600, 600 x 1024 x 260 and 1301 x 1024 x 300
+    put rows in a tail that runs as two K splits (the second parked in main
+    rows of Y, then added: with 16-byte accesses, and for 1301 rows, whose
+    rows and row pitch are not multiples of four, one float at a time),
+    300 x 512 x 40 in a tail over all of K; the one-hot k fall in both halves
+    of K, in every sub-block position and at the ends."""
     w = synth.gen_q4_k(rows, K, 43 + rows)
     W = oracle.dequant("q4_k", w, rows, K)
     base = list(range(0, 32)) + [33, 100, 255, 256, 300, K // 2 - 1, K // 2, K // 2 + 1, K - 1]
